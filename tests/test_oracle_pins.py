@@ -1,0 +1,248 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+library decoders of the storage formats, exact integer arithmetic, brute force,
+closed forms and textbook dense attention.  CPU only."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- formats
+def test_e4m3_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert nan.sum() == 2  # S.1111.111
+    assert (got[~nan] == ref[~nan]).all()
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e8m0_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.e8m0(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert (got[:255] == ref[:255]).all()
+
+
+def test_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=4000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16(b) for b in bits])
+    assert (got == ref).all()
+
+
+# ---------------------------------------------------------------- generator
+def test_generator_bounds_and_mx_exactness():
+    c = synth.Case(seed=11, B=2, n_q=2, seq_lens=[300, 130], top_k=32, H=16, idx_fmt="fp8", kv_fmt="fp8",
+                   kv_groups=5)
+    qi = c.idx_q_int()
+    assert qi.min() >= -4 and qi.max() <= 4
+    codes, scales = c.idx_q()
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    sc = torch.from_numpy(scales).view(torch.float8_e8m0fnu).double().numpy()
+    assert (dec * np.repeat(sc, 32, axis=2) == qi).all()
+    w = c.w()
+    assert (w * 32 == np.round(w * 32)).all() and w.min() >= 1 / 32 and w.max() <= 1
+    k, ks = c.k_rows(0)
+    kd = torch.from_numpy(k).view(torch.float8_e4m3fn).double().numpy()
+    assert (kd == c.k_int(0)).all() and set(np.unique(ks)) <= {0.5, 1.0}
+
+
+def test_generator_page_scatter():
+    c = synth.Case(seed=12, B=3, n_q=1, seq_lens=[200, 64, 129], top_k=8, H=16, kv_fmt="fp8", kv_groups=5)
+    bt = c.block_table()
+    kp, _ = c.k_pool()
+    lp, ls = c.latent_pool()
+    for b in range(3):
+        k, _ = c.k_rows(b)
+        lat, lats = c.latent_rows(b)
+        for s in range(int(c.seq_lens[b])):
+            pg, sl = bt[b, s // 64], s % 64
+            assert (kp[pg, sl] == k[s]).all()
+            assert (lp[pg, sl] == lat[s]).all() and (ls[pg, sl] == lats[s]).all()
+    assert sorted(bt[bt >= 0].tolist()) == list(range(c.num_pages))
+
+
+# ---------------------------------------------------------------- indexer scores
+def _exact_scores_x64(q_int, w, k_int, k_scale=None):
+    """64 * I[s] as exact integers: w = n/32, optional per-row scale in {1/2, 1}."""
+    n = np.round(w * 32).astype(np.int64)
+    dots = k_int.astype(np.int64) @ q_int.astype(np.int64).T  # [L, 64]
+    relu = np.maximum(dots, 0)
+    acc = relu @ n  # 32 * sum_h w relu(q.k)
+    mult = np.full(k_int.shape[0], 2, dtype=np.int64) if k_scale is None else np.round(2 * k_scale).astype(np.int64)
+    return acc * mult
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_scores_equal_exact_integer_arithmetic(fmt):
+    c = synth.Case(seed=21, B=1, n_q=1, seq_lens=[777], top_k=64, H=16, idx_fmt=fmt)
+    q, qs = c.idx_q()
+    w = c.w()
+    k, ks = c.k_rows(0)
+    sc = oracle.index_scores(q[0], w[0], k, 777, q_fmt=fmt, q_scales=None if qs is None else qs[0], k_fmt=fmt,
+                             k_scales=ks)
+    exact = _exact_scores_x64(c.idx_q_int()[0], w[0], c.k_int(0), ks)
+    assert (sc.astype(np.float64) * 64 == exact.astype(np.float64)).all()
+    assert exact.max() < 2 ** 24 * 2  # the fp32 sum is exact
+
+
+def test_scores_visibility_prefix():
+    c = synth.workload("decode_b1_ctx2k")
+    q, _ = c.idx_q()
+    k, _ = c.k_rows(0)
+    full = oracle.index_scores(q[0], c.w()[0], k, 2048)
+    part = oracle.index_scores(q[0], c.w()[0], k, 1000)
+    assert (full[:1000] == part).all()
+
+
+def test_golden_closed_form():
+    lines = [l for l in open(os.path.join(GOLDEN, "indexer_closed_form.txt")) if not l.startswith("#")]
+    scores = np.array([float(x) for x in lines[0].split()])
+    top4 = [int(x) for x in lines[1].split()]
+    top7 = [int(x) for x in lines[2].split()]
+    q = np.zeros((64, 128), dtype=np.float32)
+    q[0, 0], q[0, 1], q[5, 0] = 1, 2, -1
+    w = np.ones(64, dtype=np.float32)
+    w[0], w[5] = 0.5, 0.25
+    k = np.zeros((8, 128), dtype=np.float32)
+    k[:, 0] = np.arange(8) - 3
+    k[:, 1] = 1
+    to_bf16 = lambda a: torch.from_numpy(a).bfloat16().view(torch.int16).numpy().view(np.uint16)
+    sc = oracle.index_scores(to_bf16(q), w, to_bf16(k), 8)
+    assert (sc == scores).all()
+    assert oracle.topk(sc, 4)[0].tolist() == top4
+    assert oracle.topk(sc, 7)[0].tolist() == top7
+
+
+# ---------------------------------------------------------------- top-k
+def test_topk_matches_stable_argsort():
+    c = synth.workload("decode_b1_ctx2k")
+    q, _ = c.idx_q()
+    k, _ = c.k_rows(0)
+    sc = oracle.index_scores(q[0], c.w()[0], k, 2048)
+    idx, n = oracle.topk(sc, 256)
+    ref = np.argsort(-sc.astype(np.float64), kind="stable")[:256]
+    assert n == 256 and (idx == ref).all()
+
+
+def test_topk_bruteforce_with_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(30):
+        L = int(rng.integers(1, 65))
+        K = int(rng.integers(1, 70))
+        q = rng.integers(-1, 2, size=(64, 128)).astype(np.float32)
+        k = rng.integers(-1, 2, size=(L, 128)).astype(np.float32)
+        w = (rng.integers(0, 2, size=64) + 1).astype(np.float32) / 2
+        to_bf16 = lambda a: torch.from_numpy(a).bfloat16().view(torch.int16).numpy().view(np.uint16)
+        sc = oracle.index_scores(to_bf16(q), w, to_bf16(k), L)
+        idx, n = oracle.topk(sc, K)
+        assert n == min(K, L)
+        assert (idx[n:] == -1).all()
+        sel = set(idx[:n].tolist())
+        assert len(sel) == n
+        for i in sel:
+            for j in range(L):
+                if j in sel:
+                    continue
+                assert sc[i] > sc[j] or (sc[i] == sc[j] and i < j)
+
+
+def test_topk_closed_forms():
+    # all scores equal -> the K lowest positions
+    idx, n = oracle.topk(np.zeros(100, np.float32), 10)
+    assert idx.tolist() == list(range(10))
+    # strictly increasing -> the last K positions, highest first
+    idx, n = oracle.topk(np.arange(100, dtype=np.float32), 10)
+    assert idx.tolist() == list(range(99, 89, -1))
+    # K >= visible -> everything, padded with -1
+    idx, n = oracle.topk(np.array([3, 1, 2], np.float32), 5)
+    assert n == 3 and idx.tolist() == [0, 2, 1, -1, -1]
+    # negative scores are ordered too; -0.0 and +0.0 tie
+    idx, _ = oracle.topk(np.array([-1.0, -0.0, 0.0, -2.0], np.float32), 4)
+    assert idx.tolist() == [1, 2, 0, 3]
+
+
+def test_indexer_zero_query_selects_lowest_positions():
+    q = np.zeros((64, 128), np.uint16)
+    k = np.full((50, 128), 0x3F80, np.uint16)  # 1.0
+    sc = oracle.index_scores(q, np.ones(64, np.float32), k, 50)
+    assert (sc == 0).all()
+    assert oracle.topk(sc, 7)[0].tolist() == list(range(7))
+
+
+# ---------------------------------------------------------------- attention
+def _dense_attention(qd, cd, scale):
+    """Textbook softmax attention over all rows, float64."""
+    logits = scale * (qd @ cd.T)
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ cd[:, :512], (m[:, 0] + np.log(e.sum(axis=1)))
+
+
+def _bf16_to_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _decode_latent(c, cs):
+    d = torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+    G = cs.shape[1]
+    if G == 1:
+        return d * cs.astype(np.float64)
+    tile = np.minimum(np.arange(576) // 128, 4)
+    return d * cs.astype(np.float64)[:, tile]
+
+
+@pytest.mark.parametrize("kv", [("bf16", 1), ("fp8", 1), ("fp8", 5)])
+def test_sparse_with_all_positions_equals_dense(kv):
+    fmt, G = kv
+    c = synth.Case(seed=31, B=1, n_q=1, seq_lens=[300], top_k=512, H=16, kv_fmt=fmt, kv_groups=G)
+    lat, lats = c.latent_rows(0)
+    q = c.mla_q()[0]
+    rng = np.random.default_rng(1)
+    idx = np.concatenate([rng.permutation(300), -np.ones(212, int)]).astype(np.int32)
+    out, lse, p = oracle.sparse_attn(q, lat, idx, c.sm_scale, c_fmt=fmt, c_scales=lats, want_p=True)
+    cd = _bf16_to_f64(lat) if fmt == "bf16" else _decode_latent(lat, lats)
+    ref_o, ref_lse = _dense_attention(_bf16_to_f64(q), cd, c.sm_scale)
+    assert np.abs(out - ref_o).max() < 1e-12
+    assert np.abs(lse - ref_lse).max() < 1e-12
+    assert np.abs(p.sum(axis=1) - 1).max() < 1e-12
+    assert (p[:, 300:] == 0).all()
+
+
+def test_attention_special_cases():
+    c = synth.Case(seed=32, B=1, n_q=1, seq_lens=[64], top_k=8, H=4)
+    lat, _ = c.latent_rows(0)
+    q = c.mla_q()[0]
+    cd = _bf16_to_f64(lat)
+    # a single valid index -> that row, lse = its logit
+    idx = np.array([-1, 17, -1, -1], np.int32)
+    out, lse = oracle.sparse_attn(q, lat, idx, 0.1)
+    assert np.abs(out - cd[17, :512]).max() < 1e-15
+    assert np.abs(lse - 0.1 * _bf16_to_f64(q) @ cd[17]).max() < 1e-12
+    # q = 0 -> mean of the selected rows, lse = log n
+    idx = np.array([3, 9, 40, 41, 63], np.int32)
+    out, lse = oracle.sparse_attn(np.zeros_like(q), lat, idx, 0.1)
+    assert np.abs(out - cd[idx, :512].mean(axis=0)).max() < 1e-12
+    assert np.abs(lse - np.log(5)).max() < 1e-12
+    # identical rows -> that row
+    lat2 = np.repeat(lat[5:6], 64, axis=0)
+    out, _ = oracle.sparse_attn(q, lat2, idx, 0.1)
+    assert np.abs(out - cd[5, :512]).max() < 1e-12
+    # order of idx does not matter
+    out1, lse1 = oracle.sparse_attn(q, lat, idx, 0.1)
+    out2, lse2 = oracle.sparse_attn(q, lat, idx[::-1].copy(), 0.1)
+    assert np.abs(out1 - out2).max() < 1e-12 and np.abs(lse1 - lse2).max() < 1e-12
+    # nothing selected -> zeros and -inf
+    out, lse = oracle.sparse_attn(q, lat, -np.ones(4, np.int32), 0.1)
+    assert (out == 0).all() and np.isneginf(lse).all()
