@@ -1,0 +1,162 @@
+/*
+ * sparse_li.h -- C ABI of the MI355X (gfx950) sparse-attention hot path.
+ *
+ * The path has three steps, all described on the pages about the hybrid
+ * model's sparse-attention branch:
+ *   1. a lightning indexer scores every cached position of a request,
+ *        I[t,s] = sum_h w[t,h] * ReLU(q[t,h,:] . k[s,:])      (64 heads x 128)
+ *      ("Day-0 Inference Adaptation and Optimization for Hybrid Attention
+ *      Architectures", sec. 1; "Optimizing Inference for Hybrid Attention
+ *      LLMs", sec. 3.1 -- the pages name per-head scoring and a cross-head
+ *      weighted sum; the ReLU is our reading of the unnamed nonlinearity);
+ *   2. Top-K keeps the K best positions, on chip, writing back only indices
+ *      (same sections; "Day0 Inference Support and Performance Optimization
+ *      for New-Architecture LLMs", sec. 4);
+ *   3. sparse attention over the MLA latent cache reads only those rows
+ *      ("Day0 Inference Adaptation and Performance Optimization for a Sparse
+ *      Hybrid Architecture LLM", sec. 1 and 2.1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers on the current HIP device, except
+ *   where noted.  The caller owns every buffer; the library never allocates
+ *   device memory and keeps no state between calls.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *   asynchronous: buffers must stay valid until the stream has passed them.
+ * - Requests and tokens.  There are B = num_seqs requests with n_q =
+ *   q_per_seq new query tokens each, T = B*n_q tokens in all; token
+ *   t = b*n_q + j.  seq_lens[b] = L_b counts the cached positions of request b
+ *   INCLUDING its n_q new tokens, so token (b, j) sits at absolute position
+ *   L_b - n_q + j and sees positions s <= L_b - n_q + j (causal; this one rule
+ *   covers decode, multi-token verification and a prefill chunk).
+ * - Paged caches.  Position s of request b lives in physical page
+ *   block_table[b*max_pages + s/64], slot s%64; page size is 64.  Pools are
+ *   arrays of num_pages pages.  Block-table entries must lie in
+ *   [0, num_pages) and L_b <= max_pages*64; the kernels clamp out-of-range
+ *   values (so a bad table gives wrong results, never an out-of-bounds access).
+ * - Formats.  LI_BF16: bfloat16 bit patterns.  LI_FP8: OCP FP8 E4M3FN codes
+ *   with block scales (positive f32 for caches, E8M0 for the indexer query).
+ *   The pages' quantised layouts ("Optimizing Inference for Hybrid Attention
+ *   LLMs", sec. 4 table): indexer q MXFP8 with one E8M0 scale per 32
+ *   elements; FP8 caches with one f32 scale per 128-element block.
+ * - Return values: LI_OK, or a negative li_status; on failure nothing has been
+ *   enqueued and li_last_error() describes the problem (thread-local).
+ * - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SPARSE_LI_H
+#define SPARSE_LI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LI_OK = 0,
+  LI_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, top_k out of range */
+  LI_ERR_UNSUPPORTED = -2, /* shape or format this build does not implement */
+  LI_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  LI_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} li_status;
+
+typedef enum { LI_BF16 = 0, LI_FP8 = 1 } li_dtype;
+
+#define LI_PAGE_SIZE 64
+#define LI_INDEX_HEADS 64
+#define LI_INDEX_DIM 128
+#define LI_LATENT_DIM 576 /* 512 latent + 64 rope, one head shared by all query heads */
+#define LI_VALUE_DIM 512
+#define LI_MAX_TOP_K 2048
+
+/* Version string of the library (static storage). */
+const char* li_version(void);
+
+/* Message of the last failing call on this thread (static thread-local storage). */
+const char* li_last_error(void);
+
+/*
+ * Bytes of workspace li_score_topk needs for this geometry.  max_pages bounds
+ * every L_b (L_b <= max_pages*64).  Returns 0 for invalid arguments.
+ */
+size_t li_score_topk_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t top_k);
+
+/*
+ * Zero-fills a workspace on `stream` with a kernel (no hipMemset, so it may be
+ * captured in a HIP graph).  A workspace must be zero before its first use by
+ * li_score_topk; every li_score_topk call leaves it zero again.
+ */
+li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * li_score_topk -- fused indexer score + Top-K selection.
+ *
+ *   q         [T,64,128]  indexer query; LI_BF16 bits, or LI_FP8 E4M3 codes with
+ *   q_scales  [T,64,4]    E8M0 scales (one per 32 consecutive elements; LI_FP8 only,
+ *                         must be NULL for LI_BF16)
+ *   w         [T,64]      f32 per-token head weights (any sign)
+ *   k_cache   [num_pages,64,128] indexer key pool; LI_BF16 bits, or LI_FP8 codes with
+ *   k_scales  [num_pages,64]     one positive f32 scale per 128-element row (LI_FP8 only)
+ *   k_dtype must equal q_dtype.
+ *   top_k     1..2048
+ *   idx_out   [T,top_k] int32: the min(top_k, visible) positions with the largest
+ *             score, ties going to the lower position, written in ascending
+ *             position order; the rest of the row is -1.
+ *   workspace li_score_topk_workspace_size(...) bytes, zero before the first use
+ *             (see li_workspace_zero) and left zero by each call.  Calls that
+ *             share a workspace must not overlap in time.
+ *
+ * Scores live only on chip: per-chunk candidate (key, position) lists above a
+ * provable lower bound on the K-th score are the only intermediate in HBM.
+ * Supported: q_per_seq in {1, 2} (decode, two-token verification) and
+ * q_per_seq >= 3 with num_seqs == 1 (prefill chunk).
+ */
+li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                        int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q,
+                        const uint8_t* q_scales, const float* w, int32_t k_dtype, const void* k_cache,
+                        const float* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace sfa_decode / sfa_prefill need (split partial results).
+ */
+size_t sfa_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t top_k);
+
+/*
+ * sfa_decode -- sparse MLA attention over the selected latent rows.
+ *
+ *   q          [T,H,576] bf16 query (latent-absorbed 512 + rope 64), H in {16,32,64,128}
+ *   kv_cache   [num_pages,64,576] latent pool; LI_BF16 bits, or LI_FP8 codes with
+ *   kv_scales  [num_pages,64,G] positive f32 scales, G = kv_scale_groups:
+ *              1 = one scale per row, 5 = one per 128-wide tile (the 5th is 64 wide)
+ *   idx        [T,top_k] int32 logical positions of the token's request; entries
+ *              < 0 or >= L_b are skipped
+ *   sm_scale   softmax scale applied to q.c
+ *   out        [T,H,512] bf16:  sum_j softmax_j(sm_scale * q.c_j) * c_j[0:512]
+ *   lse        [T,H] f32 natural-log sum of exp of the scaled logits, or NULL;
+ *              a row with no valid index gives out = 0 and lse = -inf
+ *   workspace  sfa_workspace_size(T, H, top_k) bytes (no initialisation needed)
+ */
+li_status sfa_decode(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                     int32_t max_pages, int32_t num_pages, const void* q, int32_t num_heads, int32_t kv_dtype,
+                     const void* kv_cache, const float* kv_scales, int32_t kv_scale_groups, const int32_t* idx,
+                     int32_t top_k, float sm_scale, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * sfa_prefill -- the same operation for a prefill chunk (many query tokens of
+ * one request, each with its own index row); same arguments and layouts as
+ * sfa_decode.  It picks a launch shaped for many tokens (no index-list split).
+ */
+li_status sfa_prefill(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                      int32_t max_pages, int32_t num_pages, const void* q, int32_t num_heads, int32_t kv_dtype,
+                      const void* kv_cache, const float* kv_scales, int32_t kv_scale_groups, const int32_t* idx,
+                      int32_t top_k, float sm_scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_LI_H */

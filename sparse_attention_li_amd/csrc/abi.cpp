@@ -1,0 +1,260 @@
+// Host side of the C ABI declared in include/sparse_li.h: argument checks,
+// workspace carving, launch-shape choice.  Every check runs before anything
+// is enqueued, so a failing call leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+#include "sparse_li.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+li_status fail(li_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+li_status hip_fail(hipError_t e, const char* what) {
+  return fail(LI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Number of compute units of the current device (cached per device id).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+struct IdxLayout {
+  int chunk, ncm;
+  size_t off_counters, off_samples, off_key, off_pos, off_cnt, total;
+};
+
+IdxLayout idx_layout(int B, int n_q, int max_pages) {
+  IdxLayout l;
+  l.chunk = sli::idx_decode_chunk(B, n_q, max_pages);
+  const long long maxlen = (long long)max_pages * 64;
+  l.ncm = (int)std::max<long long>(1, (maxlen + l.chunk - 1) / l.chunk);
+  const size_t T = (size_t)B * n_q;
+  size_t o = 0;
+  l.off_counters = o;
+  o = round_up(o + (size_t)B * sli::kCounterStride * 4, 256);
+  l.off_samples = o;
+  o = round_up(o + T * l.ncm * (l.chunk / 32) * 4, 256);
+  l.off_key = o;
+  o = round_up(o + T * l.ncm * l.chunk * 4, 256);
+  l.off_pos = o;
+  o = round_up(o + T * l.ncm * l.chunk * 4, 256);
+  l.off_cnt = o;
+  o = round_up(o + T * l.ncm * 4, 256);
+  l.total = o;
+  return l;
+}
+
+// Splits of the index row so that about one workgroup per CU is busy (the
+// attention workgroup fills a CU: one wave per SIMD).
+void sfa_shape(int T, int H, int top_k, int& n_splits, int& split_len) {
+  const int cus = device_cus();
+  const int head_blocks = (H + sli::sfa_heads_per_block(H) - 1) / sli::sfa_heads_per_block(H);
+  const int per_split = T * head_blocks;
+  int s = std::max(1, (cus + per_split - 1) / per_split);
+  s = std::min(s, std::max(1, top_k / 64));
+  split_len = (top_k + s - 1) / s;
+  split_len = (split_len + 31) / 32 * 32;
+  split_len = std::min(split_len, sli::kMaxSplitRows);
+  n_splits = (top_k + split_len - 1) / split_len;
+}
+
+li_status check_paged(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                      int32_t max_pages, int32_t num_pages) {
+  if (num_seqs <= 0) return fail(LI_ERR_INVALID_ARG, "num_seqs must be positive (got %d)", num_seqs);
+  if (q_per_seq <= 0) return fail(LI_ERR_INVALID_ARG, "q_per_seq must be positive (got %d)", q_per_seq);
+  if (max_pages <= 0 || num_pages <= 0)
+    return fail(LI_ERR_INVALID_ARG, "max_pages and num_pages must be positive (got %d, %d)", max_pages, num_pages);
+  if (!seq_lens || !block_table) return fail(LI_ERR_INVALID_ARG, "seq_lens and block_table must not be NULL");
+  if ((long long)num_seqs * q_per_seq > (1LL << 30)) return fail(LI_ERR_UNSUPPORTED, "too many tokens");
+  return LI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* li_version(void) { return "sparse_li 0.1.0 (gfx950)"; }
+
+const char* li_last_error(void) { return g_err; }
+
+size_t li_score_topk_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t top_k) {
+  if (num_seqs <= 0 || q_per_seq <= 0 || max_pages <= 0 || top_k <= 0) return 0;
+  return idx_layout(num_seqs, q_per_seq, max_pages).total;
+}
+
+li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(LI_ERR_INVALID_ARG, "workspace must not be NULL");
+  if (workspace_bytes % 4 != 0 || !aligned16(workspace))
+    return fail(LI_ERR_INVALID_ARG, "workspace must be 16-byte aligned and a multiple of 4 bytes");
+  hipError_t e = sli::launch_zero_fill(workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LI_OK : hip_fail(e, "zero-fill launch");
+}
+
+li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                        int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q,
+                        const uint8_t* q_scales, const float* w, int32_t k_dtype, const void* k_cache,
+                        const float* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  li_status st = check_paged(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages);
+  if (st != LI_OK) return st;
+  if (top_k < 1 || top_k > LI_MAX_TOP_K) return fail(LI_ERR_INVALID_ARG, "top_k must be in [1, 2048] (got %d)", top_k);
+  if (!q || !w || !k_cache || !idx_out) return fail(LI_ERR_INVALID_ARG, "q, w, k_cache and idx_out must not be NULL");
+  if (q_dtype != LI_BF16 && q_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown q_dtype %d", q_dtype);
+  if (k_dtype != q_dtype) return fail(LI_ERR_UNSUPPORTED, "k_dtype must equal q_dtype (got %d, %d)", k_dtype, q_dtype);
+  const bool fp8 = q_dtype == LI_FP8;
+  if (fp8 && (!q_scales || !k_scales)) return fail(LI_ERR_INVALID_ARG, "FP8 needs q_scales and k_scales");
+  if (!fp8 && (q_scales || k_scales)) return fail(LI_ERR_INVALID_ARG, "BF16 takes no scales (pass NULL)");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w))
+    return fail(LI_ERR_INVALID_ARG, "q, w and k_cache must be 16-byte aligned");
+  if (q_per_seq > 2) return fail(LI_ERR_UNSUPPORTED, "q_per_seq %d: only 1 or 2 tokens per request are built", q_per_seq);
+  const IdxLayout l = idx_layout(num_seqs, q_per_seq, max_pages);
+  if (l.ncm > sli::kMaxChunksPerSeq)
+    return fail(LI_ERR_UNSUPPORTED, "max_pages*64 = %lld positions exceeds %d", (long long)max_pages * 64,
+                sli::kMaxChunksPerSeq * l.chunk);
+  if (!workspace) return fail(LI_ERR_WORKSPACE, "workspace must not be NULL");
+  if (workspace_bytes < l.total)
+    return fail(LI_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, l.total);
+  if (!aligned16(workspace)) return fail(LI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  sli::IdxDecodeArgs a;
+  a.B = num_seqs;
+  a.n_q = q_per_seq;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.top_k = top_k;
+  a.n_chunks_max = l.ncm;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.q = q;
+  a.q_scales = q_scales;
+  a.w = w;
+  a.k = k_cache;
+  a.k_scales = k_scales;
+  a.idx_out = idx_out;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(ws + l.off_counters);
+  a.samples = reinterpret_cast<uint32_t*>(ws + l.off_samples);
+  a.cand_key = reinterpret_cast<uint32_t*>(ws + l.off_key);
+  a.cand_pos = reinterpret_cast<int32_t*>(ws + l.off_pos);
+  a.cand_cnt = reinterpret_cast<uint32_t*>(ws + l.off_cnt);
+  hipError_t e = sli::launch_idx_decode(a, l.chunk, fp8, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LI_OK : hip_fail(e, "indexer launch");
+}
+
+size_t sfa_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t top_k) {
+  if (num_tokens <= 0 || num_heads <= 0 || top_k <= 0) return 0;
+  int s, len;
+  sfa_shape(num_tokens, num_heads, top_k, s, len);
+  if (s == 1) return 256;
+  size_t po = (size_t)num_tokens * s * num_heads * 512 * 4;
+  size_t pm = (size_t)num_tokens * s * num_heads * 2 * 4;
+  return round_up(po, 256) + round_up(pm, 256);
+}
+
+static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                            int32_t max_pages, int32_t num_pages, const void* q, int32_t num_heads, int32_t kv_dtype,
+                            const void* kv_cache, const float* kv_scales, int32_t kv_scale_groups, const int32_t* idx,
+                            int32_t top_k, float sm_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  li_status st = check_paged(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages);
+  if (st != LI_OK) return st;
+  if (top_k < 1 || top_k > LI_MAX_TOP_K) return fail(LI_ERR_INVALID_ARG, "top_k must be in [1, 2048] (got %d)", top_k);
+  if (!q || !kv_cache || !idx || !out) return fail(LI_ERR_INVALID_ARG, "q, kv_cache, idx and out must not be NULL");
+  if (num_heads != 16 && num_heads != 32 && num_heads != 64 && num_heads != 128)
+    return fail(LI_ERR_UNSUPPORTED, "num_heads must be 16, 32, 64 or 128 (got %d)", num_heads);
+  if (kv_dtype != LI_BF16 && kv_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+  const bool fp8 = kv_dtype == LI_FP8;
+  if (fp8) {
+    if (!kv_scales) return fail(LI_ERR_INVALID_ARG, "FP8 latent cache needs kv_scales");
+    if (kv_scale_groups != 1 && kv_scale_groups != 5)
+      return fail(LI_ERR_UNSUPPORTED, "kv_scale_groups must be 1 or 5 (got %d)", kv_scale_groups);
+  } else if (kv_scales) {
+    return fail(LI_ERR_INVALID_ARG, "BF16 latent cache takes no scales (pass NULL)");
+  }
+  if (!(sm_scale == sm_scale)) return fail(LI_ERR_INVALID_ARG, "sm_scale is NaN");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out))
+    return fail(LI_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+  const int T = num_seqs * q_per_seq;
+  int s, len;
+  sfa_shape(T, num_heads, top_k, s, len);
+  sli::SfaArgs a;
+  a.T = T;
+  a.n_q = q_per_seq;
+  a.H = num_heads;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.top_k = top_k;
+  a.kv_groups = fp8 ? kv_scale_groups : 1;
+  a.n_splits = s;
+  a.split_len = len;
+  a.head_blocks = (num_heads + sli::sfa_heads_per_block(num_heads) - 1) / sli::sfa_heads_per_block(num_heads);
+  a.sm_scale = sm_scale;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.q = q;
+  a.kv = kv_cache;
+  a.kv_scales = kv_scales;
+  a.idx = idx;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (s > 1) {
+    const size_t need = sfa_workspace_size(T, num_heads, top_k);
+    if (!workspace) return fail(LI_ERR_WORKSPACE, "workspace must not be NULL");
+    if (workspace_bytes < need)
+      return fail(LI_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(LI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + round_up((size_t)T * s * num_heads * 512 * 4, 256));
+  }
+  hipError_t e = sli::launch_sfa(a, fp8, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LI_OK : hip_fail(e, "attention launch");
+}
+
+li_status sfa_decode(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                     int32_t max_pages, int32_t num_pages, const void* q, int32_t num_heads, int32_t kv_dtype,
+                     const void* kv_cache, const float* kv_scales, int32_t kv_scale_groups, const int32_t* idx,
+                     int32_t top_k, float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return sfa_common(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages, q, num_heads, kv_dtype, kv_cache,
+                    kv_scales, kv_scale_groups, idx, top_k, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+li_status sfa_prefill(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                      int32_t max_pages, int32_t num_pages, const void* q, int32_t num_heads, int32_t kv_dtype,
+                      const void* kv_cache, const float* kv_scales, int32_t kv_scale_groups, const int32_t* idx,
+                      int32_t top_k, float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return sfa_common(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages, q, num_heads, kv_dtype, kv_cache,
+                    kv_scales, kv_scale_groups, idx, top_k, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

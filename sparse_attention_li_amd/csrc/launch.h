@@ -1,0 +1,54 @@
+// Internal interface between the host-side C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sli {
+
+constexpr int kCounterStride = 32;     // uint32 words per request (one 128-byte line)
+constexpr int kMaxChunksPerSeq = 256;  // positions per request <= 256 chunks
+constexpr int kMaxSplitRows = 2048;    // index entries one attention workgroup may own
+
+struct IdxDecodeArgs {
+  int B, n_q, max_pages, num_pages, top_k, n_chunks_max;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const void* q;
+  const uint8_t* q_scales;
+  const float* w;
+  const void* k;
+  const float* k_scales;
+  int32_t* idx_out;
+  // workspace
+  uint32_t* counters;  // [B][kCounterStride]: arrivals after sampling, arrivals after emission, timeouts
+  uint32_t* samples;   // [T][n_chunks_max][chunk/32]
+  uint32_t* cand_key;  // [T][n_chunks_max][chunk]
+  int32_t* cand_pos;   // [T][n_chunks_max][chunk]
+  uint32_t* cand_cnt;  // [T][n_chunks_max]
+};
+
+struct SfaArgs {
+  int T, n_q, H, max_pages, num_pages, top_k, kv_groups;
+  int n_splits, split_len, head_blocks;
+  float sm_scale;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const void* q;
+  const void* kv;
+  const float* kv_scales;
+  const int32_t* idx;
+  void* out;
+  float* lse;
+  float* part_o;   // [T][n_splits][H][512]
+  float* part_ml;  // [T][n_splits][H][2]
+};
+
+int idx_decode_chunk(int B, int n_q, int max_pages);
+hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream);
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);
+int sfa_heads_per_block(int H);
+
+}  // namespace sli

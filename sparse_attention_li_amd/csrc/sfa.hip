@@ -1,0 +1,382 @@
+// Sparse MLA attention over the selected latent rows (decode and prefill),
+// gfx950.
+//
+// What it computes ("Day0 Inference Adaptation and Performance Optimization
+// for a Sparse Hybrid Architecture LLM", sec. 1 and 2.1: attention reads only
+// the KV of the positions the indexer selected; the branch is built on MLA,
+// whose cache row is one 576-wide latent shared by every query head):
+//     l_j = sm_scale * q[t,h,:] . c[idx_j,:],   p = softmax_j(l),
+//     o[t,h,:] = sum_j p_j c[idx_j, 0:512],     lse[t,h] = log sum_j exp(l_j).
+//
+// Decomposition.  A workgroup owns one token, a block of up to 64 heads and a
+// contiguous slice of the token's index row (a "split").  Each 32-head group
+// is handled by a pair of waves, one per SIMD: for the logits each wave of the
+// pair takes half of the 576-wide contraction (and the pair adds partials
+// through LDS), for the output each takes 256 of the 512 columns, so the
+// query operands (72 VGPRs) and the fp32 output accumulators (128) stay in
+// registers for the whole slice.  Per 32-row tile:
+//   - the selected rows are gathered into LDS: bf16 rows by direct
+//     global-to-LDS loads through a three-deep ring (two tiles in flight while
+//     one is consumed), FP8 rows through registers, dequantised on the way in
+//     (block scale x E4M3 code);
+//   - logits are computed transposed, S^T[pos, head] = C_tile . q^T, on 32x32
+//     MFMA tiles.  In this layout a lane owns one head, so the running max,
+//     the running sum and the rescale of the output accumulators are per-lane
+//     scalars;
+//   - the output is accumulated transposed as well, O^T[d, head] += C^T . P^T:
+//     P^T comes straight from the S^T registers (the MFMA k-slot order is
+//     chosen to match the S^T output layout) and C^T is read from the LDS tile
+//     with the gfx950 transpose read ds_read_b64_tr_b16.
+// When a token's index row is split over several workgroups, each writes an
+// unnormalised fp32 partial and (max, sum) per head, and a combine kernel
+// merges them.
+#include "device_common.h"
+#include "launch.h"
+
+namespace sli {
+
+constexpr int kTileRows = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tile layout.  A tile holds 32 rows x 72 chunks of 16 bytes (one chunk =
+// 8 bf16).  It is cut into 36 "wave blocks": block j holds chunk j of rows
+// 0..31 followed by chunk j+36 of rows 0..31 (1024 bytes, exactly what one
+// wave-wide direct-to-LDS load writes: lane l -> row l&31, chunk j+36*(l>>5)),
+// and blocks are kBlockStride bytes apart.  The logit operand read of one
+// k-step is then two contiguous 512-byte runs, and the 64-byte skew of the
+// block stride keeps the two chunks of a transposed read on different banks.
+constexpr int kBlockStride = 1088;
+constexpr int kTileBytes = 36 * kBlockStride;
+__host__ __device__ constexpr int chunk_base(int c) { return c < 36 ? c * kBlockStride : (c - 36) * kBlockStride + 512; }
+__device__ __forceinline__ int tile_off(int row, int chunk) { return chunk_base(chunk) + 16 * row; }
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at max).
+#define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
+
+__device__ __forceinline__ void fp8x16_to_bf16(const i32x4& raw, float scale, bf16x8& lo8, bf16x8& hi8) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    auto a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[i], false);  // codes 4i, 4i+1
+    auto b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[i], true);   // codes 4i+2, 4i+3
+    bf16x8& d = i < 2 ? lo8 : hi8;
+    const int o = 4 * (i & 1);
+    d[o + 0] = (__bf16)(a[0] * scale);
+    d[o + 1] = (__bf16)(a[1] * scale);
+    d[o + 2] = (__bf16)(b[0] * scale);
+    d[o + 3] = (__bf16)(b[1] * scale);
+  }
+}
+
+// One workgroup = NW waves, wave w owns heads 32w .. 32w+31 of one token and
+// the index slice [split*split_len, ...) of that token.  One wave per SIMD:
+// the 576-wide q^T operands (144 VGPRs) and the 32x512 fp32 output
+// accumulators (256 registers) stay resident for the whole slice.
+template <int NHG, int WPH, bool FP8>
+__global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
+  constexpr int NW = NHG * WPH;     // waves
+  constexpr int KS = 36 / WPH;      // 16-wide logit k-steps per wave
+  constexpr int MI = 16 / WPH;      // 32-column output tiles per wave
+  __shared__ __attribute__((aligned(128))) char tile0[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char tile1[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char tile2[kTileBytes];
+  __shared__ int rows[kMaxSplitRows];
+  __shared__ int s_fallback;
+  __shared__ __attribute__((aligned(64))) f32x16 xbuf[WPH > 1 ? NHG * WPH : 1][kWave];
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  // Work item (split, token, head block).  Blocks are numbered so that the
+  // head blocks of one (split, token) are 8 apart: the hardware deals
+  // workgroups round-robin over the 8 XCDs, so they share an L2 and the
+  // second gather of each row hits it.
+  const int id = blockIdx.x;
+  const int hb = (id >> 3) % a.head_blocks;
+  const int rest = (id / (8 * a.head_blocks)) * 8 + (id & 7);
+  if (rest >= a.n_splits * a.T) return;
+  const int split = rest % a.n_splits, t = rest / a.n_splits;
+  const int b = t / a.n_q;
+
+  int L = a.seq_lens[b];
+  L = max(0, min(L, a.max_pages * 64));
+  const int i0 = split * a.split_len;
+  const int cnt = max(0, min(a.split_len, a.top_k - i0));
+  const int n_tiles = (cnt + kTileRows - 1) / kTileRows;
+  const int* bt = a.block_table + (size_t)b * a.max_pages;
+
+  // ---------------------------------------------------------------- rows of this slice
+  if (tid == 0) s_fallback = 0x7fffffff;
+  __syncthreads();
+  for (int i = tid; i < n_tiles * kTileRows; i += NT) {
+    int r = -1;
+    if (i < cnt) {
+      const int pos = a.idx[(size_t)t * a.top_k + i0 + i];
+      if (pos >= 0 && pos < L) {
+        int page = bt[pos >> 6];
+        page = min(max(page, 0), a.num_pages - 1);
+        r = page * 64 + (pos & 63);
+        atomicMin(&s_fallback, r);
+      }
+    }
+    rows[i] = r;
+  }
+
+  // ---------------------------------------------------------------- q^T operands
+  const int hg = wid / WPH, part = wid % WPH;
+  const int head = 32 * (NHG * hb + hg) + n;
+  const bool head_ok = head < a.H;
+  bf16x8 qb[KS];
+  {
+    const bf16x8* qp =
+        reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + ((size_t)t * a.H + (head_ok ? head : 0)) * 576);
+    const __bf16 keep = head_ok ? (__bf16)1.f : (__bf16)0.f;  // padded heads get a zero query
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qb[k] = qp[2 * (KS * part + k) + half] * keep;
+  }
+  __syncthreads();
+  const int fallback = s_fallback;
+  const bool any_valid = fallback != 0x7fffffff;
+
+  auto bufs = [&](int i) -> char* { return i == 0 ? tile0 : (i == 1 ? tile1 : tile2); };
+
+  // ---------------------------------------------------------------- gathers
+  // BF16: wave w issues the wave blocks w, w+NW, ...: lane l copies row l&31,
+  // chunks j and j+36 of the 72, so one row pointer per tile suffices.
+  constexpr int DMA_PER_WAVE = 36 / NW;
+  auto issue_dma = [&](int tile, char* dst) {
+    int pr = rows[tile * kTileRows + n];
+    pr = pr >= 0 ? pr : fallback;
+    const char* src = static_cast<const char*>(a.kv) + (size_t)pr * 1152 + 576 * half;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int j = wid + NW * i;
+      __builtin_amdgcn_global_load_lds(src + 16 * j, (lds_void*)(dst + j * kBlockStride), 16, 0, 0);
+    }
+  };
+  // FP8: codes go through registers, are scaled to bf16 and stored swizzled.
+  constexpr int F8_CHUNKS = kTileRows * 36;  // 16-code chunks per tile
+  constexpr int F8_PER = (F8_CHUNKS + NT - 1) / NT;
+  i32x4 f8_stage[FP8 ? F8_PER : 1];
+  auto load_f8 = [&](int tile) {
+#pragma unroll
+    for (int r = 0; r < F8_PER; ++r) {
+      const int f = tid + r * NT;
+      f8_stage[r] = (i32x4){0, 0, 0, 0};
+      if (f < F8_CHUNKS) {
+        const int row = f / 36, ch = f % 36;
+        const int pr = rows[tile * kTileRows + row];
+        if (pr >= 0)
+          f8_stage[r] = __builtin_nontemporal_load(
+              reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(a.kv) + (size_t)pr * 576) + ch);
+      }
+    }
+  };
+  auto store_f8 = [&](int tile, char* dst) {
+#pragma unroll
+    for (int r = 0; r < F8_PER; ++r) {
+      const int f = tid + r * NT;
+      if (f < F8_CHUNKS) {
+        const int row = f / 36, ch = f % 36;
+        const int pr = rows[tile * kTileRows + row];
+        const float sc =
+            pr >= 0 ? a.kv_scales[(size_t)pr * a.kv_groups + (a.kv_groups == 1 ? 0 : min(ch >> 3, 4))] : 0.f;
+        bf16x8 lo8, hi8;
+        fp8x16_to_bf16(f8_stage[r], sc, lo8, hi8);
+        *reinterpret_cast<bf16x8*>(dst + tile_off(row, 2 * ch)) = lo8;
+        *reinterpret_cast<bf16x8*>(dst + tile_off(row, 2 * ch + 1)) = hi8;
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  f32x16 o[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) o[i] = (f32x16){};
+  float m_run = -1e30f, l_run = 0.f;
+  const float sl2 = a.sm_scale * kLog2e;
+  const int gi = lane & 15;
+
+  const int tiles = any_valid ? n_tiles : 0;
+  if constexpr (!FP8) {
+    if (tiles > 0) issue_dma(0, bufs(0));
+    if (tiles > 1) issue_dma(1, bufs(1));
+  } else {
+    if (tiles > 0) {
+      load_f8(0);
+      store_f8(0, bufs(0));
+    }
+    __syncthreads();
+  }
+#pragma unroll 1
+  for (int tile = 0; tile < tiles; ++tile) {
+    const char* T = bufs(tile % 3);
+    if constexpr (!FP8) {
+      if (tile + 2 < tiles) {
+        issue_dma(tile + 2, bufs((tile + 2) % 3));
+        SLI_WAIT_VMCNT(2 * DMA_PER_WAVE);
+      } else if (tile + 1 < tiles) {
+        SLI_WAIT_VMCNT(DMA_PER_WAVE);
+      } else {
+        SLI_WAIT_VMCNT(0);
+      }
+      __builtin_amdgcn_s_barrier();
+    } else {
+      if (tile + 1 < tiles) load_f8(tile + 1);
+    }
+
+    // logits S^T[pos, head] over this wave's share of the 576-wide contraction
+    f32x16 s = (f32x16){};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int ks = KS * part + k;
+      // chunk 2ks+half of row n
+      const int off = ks < 18 ? ks * 2 * kBlockStride : (ks - 18) * 2 * kBlockStride + 512;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(T + off + 16 * n + kBlockStride * half);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[k], s, 0, 0, 0);
+    }
+    if constexpr (WPH > 1) {
+      xbuf[wid][lane] = s;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the partial is in LDS
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int p = 1; p < WPH; ++p) s += xbuf[hg * WPH + (part + p) % WPH][lane];
+    }
+
+    // online softmax; this lane owns head n and positions 8(v/4) + 4 half + v%4
+    float mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int pos = 8 * (v >> 2) + 4 * half + (v & 3);
+      const float x = rows[tile * kTileRows + pos] >= 0 ? s[v] * sl2 : -INFINITY;
+      s[v] = x;
+      mt = fmaxf(mt, x);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    {
+      // branch-free online-softmax update (a data-dependent branch here makes
+      // the compiler move the accumulators between register files every tile)
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    float rs = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = exp2f(s[v] - m_run);
+      rs += p;
+      pb[v >> 3][v & 7] = (__bf16)p;
+    }
+    l_run += rs + __shfl_xor(rs, 32, kWave);
+
+    // O^T[d, head] += C^T[d, pos] . P^T[pos, head].  The 16-lane group g of the
+    // wave reads rows r0..r0+3 (and r0+8..r0+11) of columns 32mi + 16(g&1) +
+    // 0..15; lane gi receives one column, four consecutive rows.
+    const int tr_lane = (2 * ((lane >> 4) & 1) + ((gi & 3) >> 1)) * kBlockStride + 16 * (4 * half + (gi >> 2)) +
+                        8 * (gi & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int m = 0; m < MI; ++m) {
+        const int mi = MI * part + m;
+        const int off = (mi < 9 ? 4 * mi * kBlockStride : (4 * mi - 36) * kBlockStride + 512) + 16 * 16 * kk;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(T + off + tr_lane));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(T + off + tr_lane + 16 * 8));
+        const bf16x8 av = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], o[m], 0, 0, 0);
+      }
+    }
+    if constexpr (FP8) {
+      if (tile + 1 < tiles) store_f8(tile + 1, bufs((tile + 1) % 3));
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+
+  // ---------------------------------------------------------------- write out
+  if (!head_ok) return;
+  const size_t th = (size_t)t * a.H + head;
+  if (a.n_splits == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    __bf16* op = static_cast<__bf16*>(a.out) + th * 512;
+#pragma unroll
+    for (int m = 0; m < MI; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * (MI * part + m) + 8 * g + 4 * half;
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[m][4 * g + i] * inv);
+        *reinterpret_cast<bf16x4*>(op + d) = v4;
+      }
+    if (a.lse && half == 0 && part == 0) a.lse[th] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    const size_t ps = ((size_t)t * a.n_splits + split) * a.H + head;
+    float* op = a.part_o + ps * 512;
+#pragma unroll
+    for (int m = 0; m < MI; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * (MI * part + m) + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(op + d) = (f32x4){o[m][4 * g], o[m][4 * g + 1], o[m][4 * g + 2], o[m][4 * g + 3]};
+      }
+    if (half == 0 && part == 0) {
+      a.part_ml[2 * ps] = m_run;
+      a.part_ml[2 * ps + 1] = l_run;
+    }
+  }
+}
+
+// Merges the split partials of one (token, head): o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(128) void sfa_combine_kernel(const SfaArgs a) {
+  const int t = blockIdx.y, h = blockIdx.x;
+  const int S = a.n_splits;
+  float M = -1e30f;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[2 * (((size_t)t * S + s) * a.H + h)]);
+  float den = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const size_t ps = ((size_t)t * S + s) * a.H + h;
+    den += exp2f(a.part_ml[2 * ps] - M) * a.part_ml[2 * ps + 1];
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int d = 4 * threadIdx.x;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const size_t ps = ((size_t)t * S + s) * a.H + h;
+    const float wgt = exp2f(a.part_ml[2 * ps] - M);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + ps * 512 + d);
+    acc += wgt * v;
+  }
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + ((size_t)t * a.H + h) * 512 + d) = r;
+  if (a.lse && threadIdx.x == 0) a.lse[(size_t)t * a.H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+template <int NHG, bool FP8>
+static hipError_t launch_sfa_one(const SfaArgs& a, hipStream_t stream) {
+  const int items = a.n_splits * a.T;
+  dim3 grid(((items + 7) / 8) * 8 * a.head_blocks);
+  hipLaunchKernelGGL((sfa_kernel<NHG, 2, FP8>), grid, dim3(NHG * 2 * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  hipLaunchKernelGGL(sfa_combine_kernel, dim3(a.H, a.T), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
+int sfa_heads_per_block(int H) { return H <= 32 ? 32 : 64; }
+
+hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream) {
+  if (a.H <= 32) return fp8 ? launch_sfa_one<1, true>(a, stream) : launch_sfa_one<1, false>(a, stream);
+  return fp8 ? launch_sfa_one<2, true>(a, stream) : launch_sfa_one<2, false>(a, stream);
+}
+
+}  // namespace sli

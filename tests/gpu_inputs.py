@@ -1,0 +1,52 @@
+"""Moves a synth.Case onto the GPU in the layouts of the C ABI (test and
+benchmark helper; no arithmetic of the method)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _t(a: np.ndarray, dev):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+class GpuCase:
+    def __init__(self, case, dev="cuda", attention=True):
+        self.case = case
+        self.dev = dev
+        self.seq_lens = _t(case.seq_lens.astype(np.int32), dev)
+        self.block_table = _t(case.block_table(), dev)
+        q, qs = case.idx_q()
+        self.q = _t(q, dev)
+        self.q_scales = None if qs is None else _t(qs, dev)
+        self.w = _t(case.w(), dev)
+        kp, ks = case.k_pool()
+        self.k_pool = _t(kp, dev)
+        self.k_scales = None if ks is None else _t(ks, dev)
+        del kp, ks
+        if attention:
+            self.mla_q = _t(case.mla_q(), dev)
+            lp, ls = case.latent_pool()
+            self.kv_pool = _t(lp, dev)
+            self.kv_scales = None if ls is None else _t(ls, dev)
+            del lp, ls
+
+    def score_topk(self, lib, **kw):
+        c = self.case
+        return lib.li_score_topk(self.q, self.w, self.k_pool, self.seq_lens, self.block_table, c.top_k,
+                                 q_scales=self.q_scales, k_scales=self.k_scales, **kw)
+
+    def attend(self, lib, idx, prefill=False, **kw):
+        c = self.case
+        fn = lib.sfa_prefill if prefill else lib.sfa_decode
+        return fn(self.mla_q, self.kv_pool, idx, self.seq_lens, self.block_table, c.sm_scale,
+                  kv_scales=self.kv_scales, **kw)
+
+
+def rel_err(out_gpu: np.ndarray, out_ref: np.ndarray) -> float:
+    """max over (token, head) of max_d |gpu - ref| / max_d |ref|."""
+    num = np.abs(out_gpu - out_ref).max(axis=-1)
+    den = np.maximum(np.abs(out_ref).max(axis=-1), 1e-30)
+    return float((num / den).max())

@@ -1,0 +1,78 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sparse_li.h, and rejects bad arguments before enqueuing."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_li_amd as li
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sparse_li.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|li_status)\s+(\w+)\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(li.EXPORTS)
+    L = li.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.li_version()
+
+
+def _call_topk(**over):
+    L = li.lib()
+    P = ctypes.c_void_p(0x10000)
+    args = dict(num_seqs=1, q_per_seq=1, seq_lens=P, bt=P, max_pages=32, num_pages=32, q_dtype=0, q=P, q_scales=None,
+                w=P, k_dtype=0, k=P, k_scales=None, top_k=256, idx=P, ws=P, ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    st = L.li_score_topk(*args.values())
+    return st, L.li_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(top_k=0), -1), (dict(top_k=2049), -1), (dict(num_seqs=0), -1), (dict(q=None), -1),
+    (dict(seq_lens=None), -1), (dict(q_dtype=7, k_dtype=7), -2), (dict(k_dtype=1), -2),
+    (dict(q_dtype=1, k_dtype=1), -1), (dict(q_scales=ctypes.c_void_p(0x10000)), -1),
+    (dict(q_per_seq=3), -2), (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(max_pages=10 ** 6), -2),
+    (dict(q=ctypes.c_void_p(0x10004)), -1),
+])
+def test_score_topk_argument_errors(over, status):
+    st, msg = _call_topk(**over)
+    assert st == status and msg
+
+
+def _call_sfa(fn="sfa_decode", **over):
+    L = li.lib()
+    P = ctypes.c_void_p(0x10000)
+    args = dict(num_seqs=1, q_per_seq=1, seq_lens=P, bt=P, max_pages=32, num_pages=32, q=P, H=128, kv_dtype=0,
+                kv=P, kv_scales=None, groups=1, idx=P, top_k=2048, sm=0.1, out=P, lse=None, ws=P,
+                ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    st = getattr(L, fn)(*args.values())
+    return st, L.li_last_error().decode()
+
+
+@pytest.mark.parametrize("fn", ["sfa_decode", "sfa_prefill"])
+@pytest.mark.parametrize("over,status", [
+    (dict(H=48), -2), (dict(H=256), -2), (dict(top_k=0), -1), (dict(idx=None), -1), (dict(kv_dtype=3), -2),
+    (dict(kv_dtype=1), -1), (dict(kv_dtype=1, kv_scales=ctypes.c_void_p(0x10000), groups=2), -2),
+    (dict(kv_scales=ctypes.c_void_p(0x10000)), -1), (dict(sm=float("nan")), -1), (dict(ws_bytes=8), -3),
+    (dict(out=ctypes.c_void_p(0x10002)), -1),
+])
+def test_sfa_argument_errors(fn, over, status):
+    st, msg = _call_sfa(fn, **over)
+    assert st == status and msg
+
+
+def test_workspace_sizes():
+    assert li.li_score_topk_workspace_size(0, 1, 1, 1) == 0
+    a = li.li_score_topk_workspace_size(32, 1, 512, 2048)
+    b = li.li_score_topk_workspace_size(32, 2, 512, 2048)
+    assert 0 < a < b
+    assert li.sfa_workspace_size(32, 128, 2048) > 0
