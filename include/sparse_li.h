@@ -103,9 +103,12 @@ li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* strea
  *   idx_out   [T,top_k] int32: the min(top_k, visible) positions with the largest
  *             score, ties going to the lower position, written in ascending
  *             position order; the rest of the row is -1.
- *   workspace li_score_topk_workspace_size(...) bytes, zero before the first use
- *             (see li_workspace_zero) and left zero by each call.  Calls that
- *             share a workspace must not overlap in time.
+ *   workspace li_score_topk_workspace_size(...) bytes, zero before its first use
+ *             (see li_workspace_zero).  Its first 512 KiB hold per-request
+ *             arrival counters at a fixed place for any geometry; each call
+ *             leaves them zero, so one workspace can serve calls of different
+ *             shapes.  Calls that share a workspace must not overlap in time.
+ *             num_seqs <= 4096.
  *
  * Scores live only on chip: per-chunk candidate (key, position) lists above a
  * provable lower bound on the K-th score are the only intermediate in HBM.

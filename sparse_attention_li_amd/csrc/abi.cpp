@@ -51,15 +51,18 @@ struct IdxLayout {
 
 IdxLayout idx_layout(int B, int n_q, int max_pages) {
   IdxLayout l;
-  l.chunk = sli::idx_decode_chunk(B, n_q, max_pages);
+  l.chunk = sli::idx_decode_chunk(B, n_q, max_pages, device_cus());
   const long long maxlen = (long long)max_pages * 64;
   l.ncm = (int)std::max<long long>(1, (maxlen + l.chunk - 1) / l.chunk);
   const size_t T = (size_t)B * n_q;
   size_t o = 0;
+  // The barrier counters sit in a fixed region at the start whatever the
+  // geometry, so a workspace reused for another batch shape never finds the
+  // previous call's samples or candidates where it expects zeroed counters.
   l.off_counters = o;
-  o = round_up(o + (size_t)B * sli::kCounterStride * 4, 256);
+  o = round_up(o + (size_t)sli::kMaxSeqs * sli::kCounterStride * 4, 256);
   l.off_samples = o;
-  o = round_up(o + T * l.ncm * (l.chunk / 32) * 4, 256);
+  o = round_up(o + T * l.ncm * (l.chunk / sli::kSampleEvery) * 4, 256);
   l.off_key = o;
   o = round_up(o + T * l.ncm * l.chunk * 4, 256);
   l.off_pos = o;
@@ -133,6 +136,7 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w))
     return fail(LI_ERR_INVALID_ARG, "q, w and k_cache must be 16-byte aligned");
   if (q_per_seq > 2) return fail(LI_ERR_UNSUPPORTED, "q_per_seq %d: only 1 or 2 tokens per request are built", q_per_seq);
+  if (num_seqs > sli::kMaxSeqs) return fail(LI_ERR_UNSUPPORTED, "num_seqs %d exceeds %d", num_seqs, sli::kMaxSeqs);
   const IdxLayout l = idx_layout(num_seqs, q_per_seq, max_pages);
   if (l.ncm > sli::kMaxChunksPerSeq)
     return fail(LI_ERR_UNSUPPORTED, "max_pages*64 = %lld positions exceeds %d", (long long)max_pages * 64,

@@ -29,12 +29,34 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 }
 
 // ---------------------------------------------------------------- scans
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS
+// round trip): Hillis-Steele inside each 16-lane row, then the row totals are
+// broadcast into the following rows.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
+    const uint32_t o = __shfl_xor(v, d, kWave);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = __shfl_xor(v, d, kWave);
+    v = v < o ? v : o;
   }
   return v;
 }
@@ -58,32 +80,68 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp,
 }
 
 // ---------------------------------------------------------------- radix select
-// Finds the k-th largest key (1 <= k <= N) among N keys given by get(i).  On
-// return every thread holds tau and n_greater = number of keys > tau (so
-// k - n_greater keys equal to tau belong to the top k).  Four 8-bit digit
-// passes with LDS histograms; wave 0 locates each digit with a suffix scan.
-// s_hist needs 256 entries, s_sel 2.
-template <class Get>
+// Finds the k-th largest key (1 <= k <= N) among N <= PER*blockDim.x keys
+// given by get(i) (any values, 0 included).  On return every thread
+// holds tau and n_greater = number of keys > tau (k - n_greater keys equal to
+// tau belong to the top k).  The keys sit in registers; a block min/max finds
+// the bits all keys share, and the select walks 8-bit windows below the
+// highest differing bit, each with one LDS histogram (plain atomics) and a
+// suffix scan by wave 0.  s_hist needs 256 entries, s_sel 4.
+template <int PER, class Get>
 __device__ uint32_t block_radix_select(Get get, int N, int k, uint32_t* s_hist, uint32_t* s_sel, int& n_greater) {
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) s_hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < N; i += blockDim.x) {
-      uint32_t key = get(i);
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave, nw = blockDim.x / kWave;
+  uint32_t key[PER];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int i = tid + r * (int)blockDim.x;
+    key[r] = i < N ? get(i) : 0u;
+    if (i < N) {
+      lo = key[r] < lo ? key[r] : lo;
+      hi = key[r] > hi ? key[r] : hi;
     }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    s_hist[2 * wid] = lo;
+    s_hist[2 * wid + 1] = hi;
+  }
+  __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0u;
+  for (int w = 0; w < nw; ++w) {
+    lo = s_hist[2 * w] < lo ? s_hist[2 * w] : lo;
+    hi = s_hist[2 * w + 1] > hi ? s_hist[2 * w + 1] : hi;
+  }
+  __syncthreads();
+  const uint32_t diff = lo ^ hi;
+  if (diff == 0) {  // all keys equal
+    n_greater = 0;
+    return lo;
+  }
+  int top = 31 - __clz(diff);           // highest bit where keys differ
+  uint32_t prefix = lo & ~((2u << top) - 1u);  // bits above it, shared by all keys
+  uint32_t remaining = (uint32_t)k;
+  while (top >= 0) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const int width = top - shift + 1;  // <= 8
+    const uint32_t above = top == 31 ? 0u : ~((2u << top) - 1u);
+    for (int i = tid; i < 256; i += blockDim.x) s_hist[i] = 0;
     __syncthreads();
-    if (threadIdx.x < kWave) {
-      const int lane = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+      if (tid + r * (int)blockDim.x < N && (key[r] & above) == prefix)
+        atomicAdd(&s_hist[(key[r] >> shift) & ((1u << width) - 1u)], 1u);
+    __syncthreads();
+    if (tid < kWave) {
       // lane l owns digits 255-4l .. 252-4l (descending)
       uint32_t h[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) h[i] = s_hist[255 - 4 * lane - i];
-      uint32_t sum = h[0] + h[1] + h[2] + h[3];
-      uint32_t incl = wave_incl_scan(sum);
-      uint32_t excl = incl - sum;
+      const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+      const uint32_t incl = wave_incl_scan(sum);
+      const uint32_t excl = incl - sum;
       if (excl < remaining && remaining <= incl) {
         uint32_t acc = excl;
 #pragma unroll
@@ -97,13 +155,95 @@ __device__ uint32_t block_radix_select(Get get, int N, int k, uint32_t* s_hist, 
       }
     }
     __syncthreads();
-    uint32_t digit = s_sel[0];
+    prefix |= s_sel[0] << shift;
     remaining = s_sel[1];
-    prefix |= digit << shift;
+    top = shift - 1;
+  }
+  n_greater = k - (int)remaining;
+  return prefix;
+}
+
+// The same selection for inputs too large to hold in registers (rare
+// fallback paths): four 8-bit passes, each streaming all N keys through get().
+template <class Get>
+__device__ uint32_t block_radix_select_big(Get get, int N, int k, uint32_t* s_hist, uint32_t* s_sel, int& n_greater) {
+  uint32_t prefix = 0, mask = 0;
+  uint32_t remaining = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) s_hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+      const uint32_t key = get(i);
+      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = s_hist[255 - 4 * lane - i];
+      const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+      const uint32_t incl = wave_incl_scan(sum);
+      const uint32_t excl = incl - sum;
+      if (excl < remaining && remaining <= incl) {
+        uint32_t acc = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (acc < remaining && remaining <= acc + h[i]) {
+            s_sel[0] = 255u - 4u * lane - i;
+            s_sel[1] = remaining - acc;
+          }
+          acc += h[i];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    remaining = s_sel[1];
     mask |= 255u << shift;
   }
   n_greater = k - (int)remaining;
   return prefix;
+}
+
+// ---------------------------------------------------------------- wave sort
+// Sorts the 64*R keys held by one wave (lane l holds elements R*l .. R*l+R-1
+// in v[0..R-1]) into descending order, in registers: bitonic network whose
+// cross-lane steps are xor-shuffles, so no LDS and no block barrier.
+template <int R>
+__device__ __forceinline__ void wave_bitonic_sort_desc(uint32_t (&v)[R]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int N = kWave * R;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if ((r & j) == 0) {
+            const int e = R * lane + r;
+            const bool desc = (e & k) == 0;
+            const uint32_t a = v[r], b = v[r | j];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[r] = sw ? b : a;
+            v[r | j] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int e = R * lane + r;
+          const uint32_t o = __shfl_xor(v[r], j / R, kWave);
+          const bool desc = (e & k) == 0;
+          const bool lower = (e & j) == 0;
+          // the lower index of a descending pair keeps the max
+          const bool keep_max = desc == lower;
+          v[r] = keep_max ? (v[r] > o ? v[r] : o) : (v[r] < o ? v[r] : o);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- bitonic sort
@@ -114,7 +254,7 @@ __device__ void lds_bitonic_sort_desc(uint32_t* s) {
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int p = threadIdx.x; p < N / 2; p += blockDim.x) {
-        const int i = 2 * j * (p / j) + (p % j);
+        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));  // j is a power of two
         const int ixj = i + j;
         uint32_t a = s[i], b = s[ixj];
         const bool desc = (i & k) == 0;
@@ -136,5 +276,37 @@ __device__ __forceinline__ uint32_t atomic_load_acquire(const uint32_t* p) {
 __device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Polling read of a counter: relaxed, so it does not invalidate caches on
+// every iteration; the caller issues one acquire fence once the wait is over.
+__device__ __forceinline__ uint32_t atomic_load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads and stores of data that other workgroups (possibly on other XCDs,
+// each with its own L2) exchange within one launch: system-coherent accesses
+// that bypass the non-coherent caches, so no reader can see a line another
+// L2 kept from an earlier launch.  Only small exchange buffers use them.
+__device__ __forceinline__ void xstore(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void xstore(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t xload(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ int32_t xload(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Waits until this wave's outstanding vector-memory operations (stores
+// included) have completed, i.e. reached L2.  Every thread runs it before the
+// workgroup barrier that precedes a single thread's agent-scope release: the
+// release writes L2 back, so all waves' stores must be in L2 by then.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
 }  // namespace sli

@@ -37,35 +37,35 @@
 
 namespace sli {
 
+typedef __attribute__((address_space(3))) void lds_void;
+#define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
+
 constexpr int kIdxThreads = 256;
-constexpr int kSampleEvery = 32;
+constexpr int kRun = 256;               // keys one wave sorts in registers
 constexpr int kCandCap = 4096;          // candidates the final select keeps in LDS
 constexpr unsigned kSpinMax = 20000;    // ~1 ms of s_sleep(2) before falling back
 
-template <int NQ, int CHUNK>
+constexpr int kSampleCap = 4096;        // samples of one request the bound search keeps in LDS
+
+// LDS: a per-wave ring of two key tiles filled by direct-to-LDS loads during
+// scoring; after scoring the same bytes hold the request's samples (bound
+// search) and, in the last workgroup, the candidates of the final select.
+template <int NQ, int CHUNK, bool FP8>
 struct IdxSmem {
-  static constexpr int kPhaseA = (NQ * CHUNK + CHUNK) * 4;
-  static constexpr int kPhaseB = kCandCap * 8;
-  static constexpr int kArena = kPhaseA > kPhaseB ? kPhaseA : kPhaseB;
+  static constexpr int kTileBytes = FP8 ? 32 * 128 : 32 * 256;
+  static constexpr int kRing = (kIdxThreads / kWave) * 2 * kTileBytes;
+  static constexpr int kReuse = kSampleCap * 4 > kCandCap * 8 ? kSampleCap * 4 : kCandCap * 8;
+  static constexpr int kArena = kRing > kReuse ? kRing : kReuse;
   alignas(16) unsigned char arena[kArena];
+  uint32_t keys[NQ * CHUNK];
   alignas(16) float w[NQ][64];
+  float kscale[FP8 ? CHUNK : 1];
+  int pages[CHUNK / 64];
   uint32_t hist[256];
   uint32_t cbase[kMaxChunksPerSeq + 1];
   uint32_t sel[2];
   uint32_t scan[8];
   uint32_t flag[4];
-};
-
-template <bool FP8>
-struct KTile;  // B-operand registers of one 32-position tile
-
-template <>
-struct KTile<false> {
-  bf16x8 v[8];
-};
-template <>
-struct KTile<true> {
-  i32x8 v[2];
 };
 
 template <bool FP8>
@@ -82,17 +82,20 @@ struct QOps<true> {
 
 template <int NQ, int CHUNK, bool FP8>
 __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeArgs a) {
-  __shared__ IdxSmem<NQ, CHUNK> sm;
-  uint32_t* s_keys = reinterpret_cast<uint32_t*>(sm.arena);   // [NQ][CHUNK]
-  uint32_t* s_sorted = s_keys + NQ * CHUNK;                    // [CHUNK]
+  __shared__ IdxSmem<NQ, CHUNK, FP8> sm;
+  uint32_t* s_keys = sm.keys;                                  // [NQ][CHUNK]
+  uint32_t* s_smp = reinterpret_cast<uint32_t*>(sm.arena);     // [kSampleCap] samples (after scoring)
 
-  constexpr int NS = CHUNK / kSampleEvery;  // samples per chunk
+  constexpr int NS = CHUNK / kSampleEvery;  // samples per chunk (CHUNK/kRun runs of kRun/kSampleEvery)
   constexpr int NT = CHUNK / 32;            // 32-position tiles per chunk
   constexpr int NW = kIdxThreads / kWave;
   static_assert(NT % NW == 0, "tiles must split evenly over waves");
+  constexpr int RUNS = CHUNK / (NW * kRun);  // sorted runs per wave
+  static_assert(RUNS * NW * kRun == CHUNK, "the chunk splits into whole runs per wave");
 
   const int c = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 31, half = lane >> 5;
 
   int L = a.seq_lens[b];
@@ -103,10 +106,19 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
   const int s0 = c * CHUNK;
   const int* bt = a.block_table + (size_t)b * a.max_pages;
 
-  // ---------------------------------------------------------------- stage q, w
+  // ---------------------------------------------------------------- stage q, w, page ids
   for (int i = tid; i < NQ * 64; i += kIdxThreads) sm.w[i / 64][i % 64] = a.w[(size_t)(t0 + i / 64) * 64 + i % 64];
+  for (int i = tid; i < CHUNK / 64; i += kIdxThreads) {
+    const int lp = s0 / 64 + i;
+    sm.pages[i] = lp * 64 < L ? min(max(bt[lp], 0), a.num_pages - 1) : 0;
+  }
+  if constexpr (FP8) {
+    __syncthreads();
+    for (int i = tid; i < CHUNK; i += kIdxThreads)
+      sm.kscale[i] = s0 + i < L ? a.k_scales[(size_t)sm.pages[i >> 6] * 64 + (i & 63)] : 0.f;
+  }
 
-  QOps<FP8> qa[NQ * 2];
+  QOps<FP8> qa[NQ * 2];  // A operands: the token's 64 heads as two 32-row tiles
 #pragma unroll
   for (int mt = 0; mt < NQ * 2; ++mt) {
     const size_t row = (size_t)(t0 + mt / 2) * 64 + 32 * (mt & 1) + n;  // (token, head)
@@ -138,56 +150,65 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
   for (int j = 0; j < NQ; ++j) vis[j] = max(0, L - NQ + j + 1);
 
   // ---------------------------------------------------------------- score
+  // Wave w scores tiles w, w+NW, ... (32 positions each, inside one page).
+  // Tiles are moved by direct-to-LDS loads into a two-slot ring private to
+  // the wave: DMA instruction i writes lane l's 16 bytes at slot + 1024 i +
+  // 16 l, and lane l copies row l&31 of the tile, 16 bytes chosen so that
+  // the MFMA B operand of k-step j is exactly what instruction j wrote
+  // (one contiguous 1 KB LDS read).  Tiles past the end of the request copy
+  // a valid (clamped) row and are masked afterwards.
+  constexpr int TB = IdxSmem<NQ, CHUNK, FP8>::kTileBytes;
+  constexpr int DMA_PER_TILE = TB / 1024;
+  constexpr int NIT = NT / NW;
+  unsigned char* ring = sm.arena + wid * 2 * TB;
   auto tile_pos0 = [&](int it) { return s0 + (wid + NW * it) * 32; };
-  auto issue = [&](int it, KTile<FP8>& kt, float& kscale) {
+  auto issue = [&](int it) {
     const int pos0 = tile_pos0(it);
-    if (pos0 >= L) return;
-    int page = bt[pos0 >> 6];
-    page = min(max(page, 0), a.num_pages - 1);
-    const size_t rowi = (size_t)page * 64 + (pos0 & 63) + n;
+    const int lp = max(min(pos0, L - 1) - s0, 0);  // position inside the chunk, clamped
+    const size_t rowi = (size_t)sm.pages[lp >> 6] * 64 + (lp & 32) + n;
+    unsigned char* dst = ring + (it & 1) * TB;
     if constexpr (!FP8) {
-      const bf16x8* kp = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.k) + rowi * 128 + 64 * half);
+      // instruction j: bytes 128 half + 16 j of the 256-byte row (k-step j)
+      const char* src = static_cast<const char*>(a.k) + rowi * 256 + 128 * half;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kt.v[j] = __builtin_nontemporal_load(kp + j);
+      for (int j = 0; j < 8; ++j) __builtin_amdgcn_global_load_lds(src + 16 * j, (lds_void*)(dst + 1024 * j), 16, 0, 0);
     } else {
-      const uint8_t* kp = static_cast<const uint8_t*>(a.k) + rowi * 128;
+      // instruction 2j+h: bytes 64 j + 32 h + 16 half (k-step j, low/high 16 codes)
+      const char* src = static_cast<const char*>(a.k) + rowi * 128 + 16 * half;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {  // same k-slot order as the query operand
-        const i32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kp + 64 * j + 16 * half));
-        const i32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kp + 64 * j + 32 + 16 * half));
-        kt.v[j] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      kscale = a.k_scales[rowi];
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(src + 64 * (i >> 1) + 32 * (i & 1), (lds_void*)(dst + 1024 * i), 16, 0, 0);
     }
   };
 
-  auto compute = [&](int it, const KTile<FP8>& kt, float kscale) {
+  auto compute = [&](int it) {
     const int tile = wid + NW * it;
     const int pos0 = s0 + tile * 32;
-    if (pos0 >= L) {
-      if (half == 0) {
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) s_keys[j * CHUNK + tile * 32 + n] = 0u;
-      }
-      return;
-    }
+    const unsigned char* src = ring + (it & 1) * TB + 16 * lane;
     f32x16 acc[NQ * 2];
 #pragma unroll
     for (int mt = 0; mt < NQ * 2; ++mt) acc[mt] = (f32x16){};
     if constexpr (!FP8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(src + 1024 * j);
 #pragma unroll
         for (int mt = 0; mt < NQ * 2; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt].v[j], kt.v[j], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt].v[j], kb, acc[mt], 0, 0, 0);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(src + 1024 * (2 * j));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(src + 1024 * (2 * j + 1));
+        const i32x8 kb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int mt = 0; mt < NQ * 2; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt].v[j], kt.v[j], acc[mt], 0, 0, 0,
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt].v[j], kb, acc[mt], 0, 0, 0,
                                                                    qa[mt].scale[j], 0, 127);
+      }
     }
+    const float kscale = FP8 ? sm.kscale[min(tile * 32 + n, CHUNK - 1)] : 1.f;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       float part = 0.f;
@@ -210,51 +231,62 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
     }
   };
 
-  {
-    KTile<FP8> kt0, kt1;
-    float ks0 = 1.f, ks1 = 1.f;
-    issue(0, kt0, ks0);
-#pragma unroll
-    for (int it = 0; it < NT / NW; it += 2) {
-      if (it + 1 < NT / NW) issue(it + 1, kt1, ks1);
-      compute(it, kt0, ks0);
-      if (it + 1 < NT / NW) {
-        if (it + 2 < NT / NW) issue(it + 2, kt0, ks0);
-        compute(it + 1, kt1, ks1);
-      }
+  issue(0);
+  if (NIT > 1) issue(1);
+#pragma unroll 1
+  for (int it = 0; it < NIT; ++it) {
+    // tile it has landed once at most the next tile's loads are outstanding
+    if (it + 1 < NIT) SLI_WAIT_VMCNT(DMA_PER_TILE);
+    else SLI_WAIT_VMCNT(0);
+    compute(it);
+    if (it + 2 < NIT) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this slot's reads are done
+      issue(it + 2);
     }
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- samples
+  // Wave w sorts runs w, w+NW, ... (kRun consecutive keys each) in registers
+  // and publishes, per run, the keys at descending ranks 16i-1, i = 1..16:
+  // each certifies that the run holds >= 16i keys >= it.
   const size_t ncm = (size_t)a.n_chunks_max;
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
-    for (int i = tid; i < CHUNK; i += kIdxThreads) s_sorted[i] = s_keys[j * CHUNK + i];
-    __syncthreads();
-    lds_bitonic_sort_desc<CHUNK>(s_sorted);
-    uint32_t* smp = a.samples + ((size_t)(t0 + j) * ncm + c) * NS;
-    for (int i = tid; i < NS; i += kIdxThreads) smp[i] = s_sorted[kSampleEvery * (i + 1) - 1];
-    __syncthreads();
+#pragma unroll 1
+    for (int r0 = 0; r0 < RUNS; ++r0) {
+      const int run = wid + NW * r0;
+      uint32_t v[kRun / kWave];
+#pragma unroll
+      for (int r = 0; r < kRun / kWave; ++r) v[r] = s_keys[j * CHUNK + kRun * run + (kRun / kWave) * lane + r];
+      wave_bitonic_sort_desc<kRun / kWave>(v);
+      // rank e = 4*lane + r; samples at e = 16i - 1, i.e. lanes 4i+3, register 3
+      uint32_t* smp = a.samples + ((size_t)(t0 + j) * ncm + c) * NS + (kRun / kSampleEvery) * run;
+      if ((lane & 3) == 3) xstore(&smp[lane >> 2], v[3]);
+    }
   }
-  uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
-  __threadfence();
+  wait_vmem();
   __syncthreads();
+  // Publish: the block barrier orders every thread's sample stores before
+  // thread 0's agent-scope release; the wait polls with relaxed loads and
+  // acquires once.  One fence pair per workgroup, not per thread or per poll.
+  uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
   if (tid == 0) {
+    fence_release_agent();
     atomic_add_acq_rel(&ctr[0], 1u);
     unsigned spins = 0, timed_out = 0;
-    while (atomic_load_acquire(&ctr[0]) < (uint32_t)n_chunks) {
+    while (atomic_load_relaxed(&ctr[0]) < (uint32_t)n_chunks) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kSpinMax) {
         timed_out = 1;
         break;
       }
     }
+    fence_acquire_agent();
     if (timed_out) atomic_add_acq_rel(&ctr[2], 1u);
     sm.flag[0] = timed_out;
   }
   __syncthreads();
-  __threadfence();
   const bool timed_out = sm.flag[0] != 0;
 
   // ---------------------------------------------------------------- lower bound and emission
@@ -267,7 +299,27 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
     if (!timed_out && m_need <= n_samples) {
       const uint32_t* smp = a.samples + (size_t)(t0 + j) * ncm * NS;
       int ngt;
-      tau = block_radix_select([&](int i) { return smp[i]; }, n_samples, m_need, sm.hist, sm.sel, ngt);
+      if (n_samples <= kSampleCap) {
+        // all loads in flight at once (a loop with one load per trip would
+        // pay the memory latency once per trip)
+        constexpr int PERS = kSampleCap / kIdxThreads;
+        uint32_t sv[PERS];
+#pragma unroll
+        for (int r = 0; r < PERS; ++r) {
+          const int i = tid + r * kIdxThreads;
+          sv[r] = i < n_samples ? xload(&smp[i]) : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < PERS; ++r) {
+          const int i = tid + r * kIdxThreads;
+          if (i < n_samples) s_smp[i] = sv[r];
+        }
+        __syncthreads();
+        tau = block_radix_select<kSampleCap / kIdxThreads>([&](int i) { return s_smp[i]; }, n_samples, m_need, sm.hist,
+                                                           sm.sel, ngt);
+      } else {
+        tau = block_radix_select_big([&](int i) { return xload(&smp[i]); }, n_samples, m_need, sm.hist, sm.sel, ngt);
+      }
       tau = max(tau, 1u);
     }
     uint32_t kk[PER];
@@ -283,28 +335,33 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (kk[i] >= tau) {
-        a.cand_key[region + off] = kk[i];
-        a.cand_pos[region + off] = s0 + tid * PER + i;
+        xstore(&a.cand_key[region + off], kk[i]);
+        xstore(&a.cand_pos[region + off], s0 + tid * PER + i);
         ++off;
       }
     }
-    if (tid == 0) a.cand_cnt[(size_t)(t0 + j) * ncm + c] = total;
+    if (tid == 0) xstore(&a.cand_cnt[(size_t)(t0 + j) * ncm + c], total);
+    __syncthreads();  // s_smp is reused by the next token's bound search
   }
-  __threadfence();
+  wait_vmem();
   __syncthreads();
-  if (tid == 0) sm.flag[1] = (atomic_add_acq_rel(&ctr[1], 1u) == (uint32_t)n_chunks - 1) ? 1u : 0u;
+  if (tid == 0) {
+    fence_release_agent();
+    const bool last = atomic_add_acq_rel(&ctr[1], 1u) == (uint32_t)n_chunks - 1;
+    if (last) fence_acquire_agent();
+    sm.flag[1] = last ? 1u : 0u;
+  }
   __syncthreads();
   if (!sm.flag[1]) return;
-  __threadfence();
 
   // ---------------------------------------------------------------- exact select (last workgroup)
-  uint32_t* s_ck = reinterpret_cast<uint32_t*>(sm.arena);  // [kCandCap]
+  uint32_t* s_ck = reinterpret_cast<uint32_t*>(sm.arena);  // [kCandCap] (the key ring is free now)
   int* s_cp = reinterpret_cast<int*>(s_ck + kCandCap);       // [kCandCap]
   const int K = a.top_k;
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
     const size_t tok = (size_t)(t0 + j);
-    uint32_t cc = tid < n_chunks ? a.cand_cnt[tok * ncm + tid] : 0u;
+    uint32_t cc = tid < n_chunks ? xload(&a.cand_cnt[tok * ncm + tid]) : 0u;
     uint32_t N;
     uint32_t base = block_excl_scan(cc, sm.scan, N);
     if (tid < n_chunks) sm.cbase[tid] = base;
@@ -321,44 +378,74 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
     };
     const bool in_lds = N <= (uint32_t)kCandCap;
     if (in_lds) {
-      for (int f = tid; f < (int)N; f += kIdxThreads) {
-        size_t g = locate(f);
-        s_ck[f] = a.cand_key[g];
-        s_cp[f] = a.cand_pos[g];
+      // all addresses first, then all loads in flight at once
+      constexpr int PERT = kCandCap / kIdxThreads;
+      size_t gaddr[PERT];
+#pragma unroll
+      for (int r = 0; r < PERT; ++r) {
+        const int f = tid + r * kIdxThreads;
+        gaddr[r] = f < (int)N ? locate(f) : 0;
+      }
+      uint32_t kv[PERT];
+      int32_t pv[PERT];
+#pragma unroll
+      for (int r = 0; r < PERT; ++r) {
+        const int f = tid + r * kIdxThreads;
+        kv[r] = f < (int)N ? xload(&a.cand_key[gaddr[r]]) : 0u;
+        pv[r] = f < (int)N ? xload(&a.cand_pos[gaddr[r]]) : -1;
+      }
+#pragma unroll
+      for (int r = 0; r < PERT; ++r) {
+        const int f = tid + r * kIdxThreads;
+        if (f < (int)N) {
+          s_ck[f] = kv[r];
+          s_cp[f] = pv[r];
+        }
       }
       __syncthreads();
     }
-    auto key_at = [&](int f) { return in_lds ? s_ck[f] : a.cand_key[locate(f)]; };
-    auto pos_at = [&](int f) { return in_lds ? s_cp[f] : a.cand_pos[locate(f)]; };
+    auto key_at = [&](int f) { return in_lds ? s_ck[f] : xload(&a.cand_key[locate(f)]); };
+    auto pos_at = [&](int f) { return in_lds ? s_cp[f] : xload(&a.cand_pos[locate(f)]); };
 
     uint32_t tau = 0u;
     int ties = 0;
     const bool take_all = N <= (uint32_t)K;
     if (!take_all) {
       int ngt;
-      tau = block_radix_select(key_at, (int)N, K, sm.hist, sm.sel, ngt);
+      tau = in_lds ? block_radix_select<kCandCap / kIdxThreads>(key_at, (int)N, K, sm.hist, sm.sel, ngt)
+                   : block_radix_select_big(key_at, (int)N, K, sm.hist, sm.sel, ngt);
       ties = K - ngt;
     }
     int32_t* out = a.idx_out + tok * K;
-    uint32_t written = 0, ties_seen = 0;
-    for (int f0 = 0; f0 < (int)N; f0 += kIdxThreads) {
-      const int f = f0 + tid;
-      uint32_t key = 0;
-      int pos = -1;
-      if (f < (int)N) {
-        key = key_at(f);
-        pos = pos_at(f);
+    // Each thread walks a contiguous segment of the (position-ordered)
+    // candidates: one scan ranks the ties at tau, one places the selected.
+    const int seg = ((int)N + kIdxThreads - 1) / kIdxThreads;
+    const int f_lo = min((int)N, tid * seg), f_hi = min((int)N, f_lo + seg);
+    uint32_t my_ties = 0;
+    if (!take_all)
+      for (int f = f_lo; f < f_hi; ++f) my_ties += key_at(f) == tau ? 1u : 0u;
+    uint32_t tie_tot;
+    uint32_t tie_rank = block_excl_scan(my_ties, sm.scan, tie_tot);
+    uint32_t my_sel = 0;
+    {
+      uint32_t tr = tie_rank;
+      for (int f = f_lo; f < f_hi; ++f) {
+        const uint32_t key = key_at(f);
+        const bool tie = !take_all && key == tau;
+        my_sel += (take_all || key > tau || (tie && tr < (uint32_t)ties)) ? 1u : 0u;
+        tr += tie ? 1u : 0u;
       }
-      const bool valid = f < (int)N;
-      uint32_t is_tie = (valid && !take_all && key == tau) ? 1u : 0u;
-      uint32_t nt_tot;
-      uint32_t tie_rank = ties_seen + block_excl_scan(is_tie, sm.scan, nt_tot);
-      const bool sel = valid && (take_all || key > tau || (is_tie && tie_rank < (uint32_t)ties));
-      uint32_t ns_tot;
-      uint32_t o = written + block_excl_scan(sel ? 1u : 0u, sm.scan, ns_tot);
-      if (sel) out[o] = pos;
-      written += ns_tot;
-      ties_seen += nt_tot;
+    }
+    uint32_t written;
+    uint32_t o = block_excl_scan(my_sel, sm.scan, written);
+    {
+      uint32_t tr = tie_rank;
+      for (int f = f_lo; f < f_hi; ++f) {
+        const uint32_t key = key_at(f);
+        const bool tie = !take_all && key == tau;
+        if (take_all || key > tau || (tie && tr < (uint32_t)ties)) out[o++] = pos_at(f);
+        tr += tie ? 1u : 0u;
+      }
     }
     for (int i = (int)written + tid; i < K; i += kIdxThreads) out[i] = -1;
     __syncthreads();
@@ -376,17 +463,25 @@ static hipError_t launch_one(const IdxDecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int idx_decode_chunk(int B, int n_q, int max_pages) {
-  (void)B;
+// Positions per workgroup.  Larger chunks when the grid would not otherwise
+// fit on the chip at once (two workgroups per CU): with every workgroup of a
+// request resident, the cross-workgroup bound, the candidate exchange and the
+// final select run after the streaming instead of under its memory latency.
+int idx_decode_chunk(int B, int n_q, int max_pages, int cus) {
   (void)n_q;
-  (void)max_pages;
-  return 1024;
+  const long long maxlen = (long long)max_pages * 64;
+  const long long wgs1k = (long long)B * ((maxlen + 1023) / 1024);
+  return wgs1k > 2LL * cus ? 2048 : 1024;
 }
 
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream) {
-  if (chunk != 1024) return hipErrorInvalidValue;
-  if (a.n_q == 1) return fp8 ? launch_one<1, 1024, true>(a, stream) : launch_one<1, 1024, false>(a, stream);
-  if (a.n_q == 2) return fp8 ? launch_one<2, 1024, true>(a, stream) : launch_one<2, 1024, false>(a, stream);
+  if (chunk == 1024) {
+    if (a.n_q == 1) return fp8 ? launch_one<1, 1024, true>(a, stream) : launch_one<1, 1024, false>(a, stream);
+    if (a.n_q == 2) return fp8 ? launch_one<2, 1024, true>(a, stream) : launch_one<2, 1024, false>(a, stream);
+  } else if (chunk == 2048) {
+    if (a.n_q == 1) return fp8 ? launch_one<1, 2048, true>(a, stream) : launch_one<1, 2048, false>(a, stream);
+    if (a.n_q == 2) return fp8 ? launch_one<2, 2048, true>(a, stream) : launch_one<2, 2048, false>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -8,8 +8,10 @@
 namespace sli {
 
 constexpr int kCounterStride = 32;     // uint32 words per request (one 128-byte line)
+constexpr int kMaxSeqs = 4096;         // requests per call; sizes the fixed counter region
 constexpr int kMaxChunksPerSeq = 256;  // positions per request <= 256 chunks
 constexpr int kMaxSplitRows = 2048;    // index entries one attention workgroup may own
+constexpr int kSampleEvery = 16;       // indexer: one order-statistic sample per 16 ranks
 
 struct IdxDecodeArgs {
   int B, n_q, max_pages, num_pages, top_k, n_chunks_max;
@@ -23,7 +25,7 @@ struct IdxDecodeArgs {
   int32_t* idx_out;
   // workspace
   uint32_t* counters;  // [B][kCounterStride]: arrivals after sampling, arrivals after emission, timeouts
-  uint32_t* samples;   // [T][n_chunks_max][chunk/32]
+  uint32_t* samples;   // [T][n_chunks_max][chunk/kSampleEvery]
   uint32_t* cand_key;  // [T][n_chunks_max][chunk]
   int32_t* cand_pos;   // [T][n_chunks_max][chunk]
   uint32_t* cand_cnt;  // [T][n_chunks_max]
@@ -45,7 +47,7 @@ struct SfaArgs {
   float* part_ml;  // [T][n_splits][H][2]
 };
 
-int idx_decode_chunk(int B, int n_q, int max_pages);
+int idx_decode_chunk(int B, int n_q, int max_pages, int cus);
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);

@@ -165,3 +165,19 @@ def test_decode_b32_ctx32k_sampled(li):
     idx = idx.cpu().numpy()
     _check_indices(case, idx, tokens, ores)
     _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
+
+
+def test_repeated_calls_identical_many_chunks(li):
+    """Regression test for cross-workgroup publication: candidates written by
+    workgroups on other XCDs must be visible to the one that runs the final
+    select.  Many requests x many chunks, repeated; every call must equal the
+    oracle-checked first call."""
+    case = synth.Case(seed=18, B=24, n_q=1, seq_lens=[9000 + 731 * b for b in range(24)], top_k=1, H=16)
+    g = GpuCase(case, attention=False)
+    first = g.score_topk(li).clone()
+    for _ in range(20):
+        assert torch.equal(g.score_topk(li), first)
+    case2 = synth.Case(seed=18, B=24, n_q=1, seq_lens=case.seq_lens, top_k=1, H=16)
+    ores = oracle.run_tokens(case2, [0, 23], with_attn=False)
+    fi = first.cpu().numpy()
+    _check_indices(case, fi, [0, 23], ores)
