@@ -152,46 +152,53 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
   // ---------------------------------------------------------------- score
   // Wave w scores tiles w, w+NW, ... (32 positions each, inside one page).
   // Tiles are moved by direct-to-LDS loads into a two-slot ring private to
-  // the wave: DMA instruction i writes lane l's 16 bytes at slot + 1024 i +
-  // 16 l, and lane l copies row l&31 of the tile, 16 bytes chosen so that
-  // the MFMA B operand of k-step j is exactly what instruction j wrote
-  // (one contiguous 1 KB LDS read).  Tiles past the end of the request copy
-  // a valid (clamped) row and are masked afterwards.
+  // the wave.  Each DMA instruction reads one contiguous kilobyte of the tile
+  // (eight lanes per 128-byte line) and writes lane l's 16 bytes to slot
+  // 64i + l; inside a line the 16-byte chunks are XOR-swizzled by (row & 7),
+  // so the MFMA operand reads (row n, fixed column) hit distinct banks.
+  // Tiles past the end of the request copy a valid (clamped) tile and are
+  // masked afterwards.
   constexpr int TB = IdxSmem<NQ, CHUNK, FP8>::kTileBytes;
   constexpr int DMA_PER_TILE = TB / 1024;
   constexpr int NIT = NT / NW;
+  constexpr int ROW = FP8 ? 128 : 256;             // bytes per key row
+  constexpr int RPI = 1024 / ROW;                  // rows per DMA instruction
   unsigned char* ring = sm.arena + wid * 2 * TB;
   auto tile_pos0 = [&](int it) { return s0 + (wid + NW * it) * 32; };
+  // this lane's share of every DMA instruction: row (within the instruction)
+  // and the 16-byte chunk of that row
+  const int dma_row = lane / (64 / RPI);
+  const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
   auto issue = [&](int it) {
     const int pos0 = tile_pos0(it);
     const int lp = max(min(pos0, L - 1) - s0, 0);  // position inside the chunk, clamped
-    const size_t rowi = (size_t)sm.pages[lp >> 6] * 64 + (lp & 32) + n;
+    const char* base =
+        static_cast<const char*>(a.k) + ((size_t)sm.pages[lp >> 6] * 64 + (lp & 32)) * ROW;
     unsigned char* dst = ring + (it & 1) * TB;
-    if constexpr (!FP8) {
-      // instruction j: bytes 128 half + 16 j of the 256-byte row (k-step j)
-      const char* src = static_cast<const char*>(a.k) + rowi * 256 + 128 * half;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) __builtin_amdgcn_global_load_lds(src + 16 * j, (lds_void*)(dst + 1024 * j), 16, 0, 0);
-    } else {
-      // instruction 2j+h: bytes 64 j + 32 h + 16 half (k-step j, low/high 16 codes)
-      const char* src = static_cast<const char*>(a.k) + rowi * 128 + 16 * half;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(src + 64 * (i >> 1) + 32 * (i & 1), (lds_void*)(dst + 1024 * i), 16, 0, 0);
+    for (int i = 0; i < DMA_PER_TILE; ++i) {
+      const int row = RPI * i + dma_row;
+      const int col = 8 * dma_line + ((lane & 7) ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
     }
+  };
+  // LDS byte offset of (row, 16-byte chunk) inside a tile
+  auto slot = [&](int row, int col) {
+    return 1024 * (row / RPI) + 16 * ((64 / RPI) * (row % RPI) + 8 * (col >> 3) + ((col & 7) ^ (row & 7)));
   };
 
   auto compute = [&](int it) {
     const int tile = wid + NW * it;
     const int pos0 = s0 + tile * 32;
-    const unsigned char* src = ring + (it & 1) * TB + 16 * lane;
+    const unsigned char* src = ring + (it & 1) * TB;
     f32x16 acc[NQ * 2];
 #pragma unroll
     for (int mt = 0; mt < NQ * 2; ++mt) acc[mt] = (f32x16){};
     if constexpr (!FP8) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(src + 1024 * j);
+        // k-step j: row n, bytes 128 half + 16 j = chunk 8 half + j
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(src + slot(n, 8 * half + j));
 #pragma unroll
         for (int mt = 0; mt < NQ * 2; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt].v[j], kb, acc[mt], 0, 0, 0);
@@ -199,8 +206,9 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(src + 1024 * (2 * j));
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(src + 1024 * (2 * j + 1));
+        // k-step j: row n, bytes 64 j + 16 half (chunk 4j + half) and 64 j + 32 + 16 half
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(src + slot(n, 4 * j + half));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(src + slot(n, 4 * j + 2 + half));
         const i32x8 kb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int mt = 0; mt < NQ * 2; ++mt)

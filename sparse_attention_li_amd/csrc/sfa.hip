@@ -43,16 +43,18 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS tile layout.  A tile holds 32 rows x 72 chunks of 16 bytes (one chunk =
-// 8 bf16).  It is cut into 36 "wave blocks": block j holds chunk j of rows
-// 0..31 followed by chunk j+36 of rows 0..31 (1024 bytes, exactly what one
-// wave-wide direct-to-LDS load writes: lane l -> row l&31, chunk j+36*(l>>5)),
-// and blocks are kBlockStride bytes apart.  The logit operand read of one
-// k-step is then two contiguous 512-byte runs, and the 64-byte skew of the
-// block stride keeps the two chunks of a transposed read on different banks.
-constexpr int kBlockStride = 1088;
-constexpr int kTileBytes = 36 * kBlockStride;
-__host__ __device__ constexpr int chunk_base(int c) { return c < 36 ? c * kBlockStride : (c - 36) * kBlockStride + 512; }
-__device__ __forceinline__ int tile_off(int row, int chunk) { return chunk_base(chunk) + 16 * row; }
+// 8 bf16), 36 KiB, filled by 36 wave-wide direct-to-LDS loads.  Load i copies
+// one 128-byte line (chunks 8g..8g+7, g = i/4) of the eight rows 8(i%4)..+7:
+// eight lanes per row, so every load reads whole cache lines.  Lane l of load
+// i lands at byte 16(64i + l); inside its row the chunk is placed at
+// position (chunk & 7) ^ f(row), a swizzle under which both operand reads are
+// conflict-free: the logit operand read (eight rows, one chunk) and the
+// transposed read (four consecutive rows, two adjacent chunks).
+constexpr int kTileBytes = 36 * 1024;
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return 16 * (64 * (4 * (chunk >> 3) + (row >> 3)) + 8 * (row & 7) + ((chunk & 7) ^ swz(row)));
+}
 
 // s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at max).
 #define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
@@ -143,17 +145,19 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
   auto bufs = [&](int i) -> char* { return i == 0 ? tile0 : (i == 1 ? tile1 : tile2); };
 
   // ---------------------------------------------------------------- gathers
-  // BF16: wave w issues the wave blocks w, w+NW, ...: lane l copies row l&31,
-  // chunks j and j+36 of the 72, so one row pointer per tile suffices.
+  // BF16: wave w issues loads w, w+NW, ... of the tile; lane l copies row
+  // 8(i%4) + l/8, chunk 8(i/4) + ((l & 7) ^ f(row)).
   constexpr int DMA_PER_WAVE = 36 / NW;
   auto issue_dma = [&](int tile, char* dst) {
-    int pr = rows[tile * kTileRows + n];
-    pr = pr >= 0 ? pr : fallback;
-    const char* src = static_cast<const char*>(a.kv) + (size_t)pr * 1152 + 576 * half;
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int j = wid + NW * i;
-      __builtin_amdgcn_global_load_lds(src + 16 * j, (lds_void*)(dst + j * kBlockStride), 16, 0, 0);
+    for (int k = 0; k < DMA_PER_WAVE; ++k) {
+      const int i = wid + NW * k;
+      const int row = 8 * (i & 3) + (lane >> 3);
+      const int chunk = 8 * (i >> 2) + ((lane & 7) ^ swz(row));
+      int pr = rows[tile * kTileRows + row];
+      pr = pr >= 0 ? pr : fallback;
+      const char* src = static_cast<const char*>(a.kv) + (size_t)pr * 1152 + 16 * chunk;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * i), 16, 0, 0);
     }
   };
   // FP8: codes go through registers, are scaled to bf16 and stored swizzled.
@@ -228,15 +232,14 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     }
 
     // logits S^T[pos, head] over this wave's share of the 576-wide contraction
+    // all operand reads are issued before the MFMA chain (one wave per SIMD:
+    // nothing else would hide the LDS latency)
+    bf16x8 av[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) av[k] = *reinterpret_cast<const bf16x8*>(T + tile_off(n, 2 * (KS * part + k) + half));
     f32x16 s = (f32x16){};
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const int ks = KS * part + k;
-      // chunk 2ks+half of row n
-      const int off = ks < 18 ? ks * 2 * kBlockStride : (ks - 18) * 2 * kBlockStride + 512;
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(T + off + 16 * n + kBlockStride * half);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[k], s, 0, 0, 0);
-    }
+    for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s, 0, 0, 0);
     if constexpr (WPH > 1) {
       xbuf[wid][lane] = s;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the partial is in LDS
@@ -275,21 +278,24 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     }
     l_run += rs + __shfl_xor(rs, 32, kWave);
 
-    // O^T[d, head] += C^T[d, pos] . P^T[pos, head].  The 16-lane group g of the
-    // wave reads rows r0..r0+3 (and r0+8..r0+11) of columns 32mi + 16(g&1) +
-    // 0..15; lane gi receives one column, four consecutive rows.
-    const int tr_lane = (2 * ((lane >> 4) & 1) + ((gi & 3) >> 1)) * kBlockStride + 16 * (4 * half + (gi >> 2)) +
-                        8 * (gi & 1);
+    // O^T[d, head] += C^T[d, pos] . P^T[pos, head].  The 16-lane group of the
+    // wave reads rows r0..r0+3 (and r0+8..r0+11) of columns 32mi + 16((lane>>4)&1)
+    // + 0..15 (two chunks); lane gi receives one column, four consecutive rows.
+    const int tr_row = 4 * half + (gi >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      bf16x4 lo[MI], hi[MI];
 #pragma unroll
       for (int m = 0; m < MI; ++m) {
-        const int mi = MI * part + m;
-        const int off = (mi < 9 ? 4 * mi * kBlockStride : (4 * mi - 36) * kBlockStride + 512) + 16 * 16 * kk;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(T + off + tr_lane));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(T + off + tr_lane + 16 * 8));
-        const bf16x8 av = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], o[m], 0, 0, 0);
+        const int r0 = 16 * kk + tr_row, c0 = 4 * (MI * part + m) + tr_chunk;
+        lo[m] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(T + tile_off(r0, c0) + 8 * (gi & 1)));
+        hi[m] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(T + tile_off(r0 + 8, c0) + 8 * (gi & 1)));
+      }
+#pragma unroll
+      for (int m = 0; m < MI; ++m) {
+        const bf16x8 cv = (bf16x8){lo[m][0], lo[m][1], lo[m][2], lo[m][3], hi[m][0], hi[m][1], hi[m][2], hi[m][3]};
+        o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv, pb[kk], o[m], 0, 0, 0);
       }
     }
     if constexpr (FP8) {
