@@ -108,6 +108,7 @@ const char* li_last_error(void) { return g_err; }
 
 size_t li_score_topk_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t top_k) {
   if (num_seqs <= 0 || q_per_seq <= 0 || max_pages <= 0 || top_k <= 0) return 0;
+  if (q_per_seq > 2) return 256;  // the prefill kernel keeps its selection state in LDS
   return idx_layout(num_seqs, q_per_seq, max_pages).total;
 }
 
@@ -135,7 +136,29 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
   if (!fp8 && (q_scales || k_scales)) return fail(LI_ERR_INVALID_ARG, "BF16 takes no scales (pass NULL)");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w))
     return fail(LI_ERR_INVALID_ARG, "q, w and k_cache must be 16-byte aligned");
-  if (q_per_seq > 2) return fail(LI_ERR_UNSUPPORTED, "q_per_seq %d: only 1 or 2 tokens per request are built", q_per_seq);
+  if (q_per_seq > 2) {
+    // prefill chunk: many causal queries per request, selection state on chip
+    if (fp8) return fail(LI_ERR_UNSUPPORTED, "the prefill indexer is built for bf16 only");
+    if (max_pages > sli::kMaxPrefillPages)
+      return fail(LI_ERR_UNSUPPORTED, "prefill: max_pages %d exceeds %d", max_pages, sli::kMaxPrefillPages);
+    if ((long long)num_seqs * ((q_per_seq + 3) / 4) > 0x7fffffffLL) return fail(LI_ERR_UNSUPPORTED, "grid too large");
+    sli::IdxPrefillArgs pa;
+    pa.B = num_seqs;
+    pa.n_q = q_per_seq;
+    pa.max_pages = max_pages;
+    pa.num_pages = num_pages;
+    pa.top_k = top_k;
+    pa.seq_lens = seq_lens;
+    pa.block_table = block_table;
+    pa.q = q;
+    pa.w = w;
+    pa.k = k_cache;
+    pa.idx_out = idx_out;
+    (void)workspace;
+    (void)workspace_bytes;
+    hipError_t e = sli::launch_idx_prefill(pa, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LI_OK : hip_fail(e, "prefill indexer launch");
+  }
   if (num_seqs > sli::kMaxSeqs) return fail(LI_ERR_UNSUPPORTED, "num_seqs %d exceeds %d", num_seqs, sli::kMaxSeqs);
   const IdxLayout l = idx_layout(num_seqs, q_per_seq, max_pages);
   if (l.ncm > sli::kMaxChunksPerSeq)

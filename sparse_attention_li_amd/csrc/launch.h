@@ -31,6 +31,18 @@ struct IdxDecodeArgs {
   uint32_t* cand_cnt;  // [T][n_chunks_max]
 };
 
+constexpr int kMaxPrefillPages = 4096;  // prefill: positions per request <= 4096 pages
+
+struct IdxPrefillArgs {
+  int B, n_q, max_pages, num_pages, top_k;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const void* q;
+  const float* w;
+  const void* k;
+  int32_t* idx_out;
+};
+
 struct SfaArgs {
   int T, n_q, H, max_pages, num_pages, top_k, kv_groups;
   int n_splits, split_len, head_blocks;
@@ -50,6 +62,7 @@ struct SfaArgs {
 int idx_decode_chunk(int B, int n_q, int max_pages, int cus);
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);
 int sfa_heads_per_block(int H);
 

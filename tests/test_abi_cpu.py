@@ -39,7 +39,9 @@ def _call_topk(**over):
     (dict(top_k=0), -1), (dict(top_k=2049), -1), (dict(num_seqs=0), -1), (dict(q=None), -1),
     (dict(seq_lens=None), -1), (dict(q_dtype=7, k_dtype=7), -2), (dict(k_dtype=1), -2),
     (dict(q_dtype=1, k_dtype=1), -1), (dict(q_scales=ctypes.c_void_p(0x10000)), -1),
-    (dict(q_per_seq=3), -2), (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(max_pages=10 ** 6), -2),
+    (dict(q_per_seq=3, q_dtype=1, k_dtype=1, q_scales=ctypes.c_void_p(0x10000),
+          k_scales=ctypes.c_void_p(0x10000)), -2),
+    (dict(q_per_seq=3, max_pages=5000), -2), (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(max_pages=10 ** 6), -2),
     (dict(q=ctypes.c_void_p(0x10004)), -1),
 ])
 def test_score_topk_argument_errors(over, status):

@@ -60,6 +60,10 @@ SMALL = {
                    kv_groups=1),
     "fp8_g5_mtp2": dict(seed=13, B=2, n_q=2, seq_lens=[3000, 700], top_k=256, H=128, idx_fmt="fp8",
                         kv_fmt="fp8", kv_groups=5),
+    # prefill chunks (many causal queries per request)
+    "prefill_ragged": dict(seed=19, B=1, n_q=37, seq_lens=[300], top_k=64, H=16),
+    "prefill_k_gt_visible": dict(seed=20, B=2, n_q=9, seq_lens=[40, 200], top_k=128, H=32),
+    "prefill_compactions": dict(seed=21, B=1, n_q=12, seq_lens=[9000], top_k=512, H=64),
 }
 
 
@@ -181,3 +185,25 @@ def test_repeated_calls_identical_many_chunks(li):
     ores = oracle.run_tokens(case2, [0, 23], with_attn=False)
     fi = first.cpu().numpy()
     _check_indices(case, fi, [0, 23], ores)
+
+
+def test_prefill_all_equal_scores(li):
+    case = synth.Case(seed=22, B=1, n_q=8, seq_lens=[5000], top_k=700, H=16)
+    g = GpuCase(case, attention=False)
+    g.q = torch.zeros_like(g.q)
+    idx = g.score_topk(li).cpu().numpy()
+    assert (idx == np.arange(700)[None, :]).all()
+
+
+def test_prefill_4k_on_64k_sampled(li):
+    """Full-size prefill chunk: 4096 causal queries on a 65536-token cache;
+    sampled queries (first, last and spread) checked against the oracle."""
+    case = synth.workload("prefill_4k_on_64k")
+    g = GpuCase(case)
+    idx = g.score_topk(li)
+    out, lse = g.attend(li, idx, prefill=True)
+    torch.cuda.synchronize()
+    tokens = [0, 1, 1365, 2730, 4095]
+    ores = oracle.run_tokens(case, tokens)
+    _check_indices(case, idx.cpu().numpy(), tokens, ores)
+    _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
