@@ -113,8 +113,8 @@ li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* strea
  * Scores live only on chip: per-chunk candidate (key, position) lists above a
  * provable lower bound on the K-th score are the only intermediate in HBM.
  * Supported: q_per_seq in {1, 2} (decode, two-token verification; bf16 or
- * FP8) and q_per_seq >= 3 (prefill chunk; bf16, max_pages <= 4096, the
- * workspace is not used and may be NULL).
+ * FP8) and q_per_seq >= 3 (prefill chunk; bf16, the workspace is not used
+ * and may be NULL).
  */
 li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                         int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q,

@@ -139,8 +139,6 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
   if (q_per_seq > 2) {
     // prefill chunk: many causal queries per request, selection state on chip
     if (fp8) return fail(LI_ERR_UNSUPPORTED, "the prefill indexer is built for bf16 only");
-    if (max_pages > sli::kMaxPrefillPages)
-      return fail(LI_ERR_UNSUPPORTED, "prefill: max_pages %d exceeds %d", max_pages, sli::kMaxPrefillPages);
     if ((long long)num_seqs * ((q_per_seq + 3) / 4) > 0x7fffffffLL) return fail(LI_ERR_UNSUPPORTED, "grid too large");
     sli::IdxPrefillArgs pa;
     pa.B = num_seqs;

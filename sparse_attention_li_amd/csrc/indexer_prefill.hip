@@ -8,24 +8,31 @@
 // query j of request b sees positions s <= L_b - n_q + j.
 //
 // Decomposition.  A workgroup owns 4 consecutive queries of one request and
-// streams every key position any of them can see.  Each query is handled by
-// a pair of waves, one per half of the 64 indexer heads (MFMA rows), and the
-// 8 waves share each 32-position key tile: it is moved once into an LDS ring
-// by direct-to-LDS loads (one 1 KiB instruction per wave), so key traffic
-// from L2 is divided by the number of queries in flight.  Workgroups on the
-// same XCD stream the same positions at about the same time and share them
-// through L2; query blocks are scheduled heaviest (latest) first.
+// streams every key position any of them can see, one 64-position page per
+// step.  The page is moved once into an LDS ring by direct-to-LDS loads (two
+// 1 KiB instructions per wave) and read by all 8 waves: wave (query, half)
+// multiplies all 64 heads of its query (two 32-row MFMA blocks, q held in
+// registers) with the 32 positions of its half of the page, so key traffic
+// from L2 is divided by the 4 queries and no partial head sums cross waves
+// inside a page.  The weighted ReLU head sum of page t (head weights in
+// registers) is taken while the MFMAs of page t+1 run, so the vector work
+// hides behind the matrix cores.  The two lane halves of each wave hold
+// different heads; their partial sums go to LDS and the query's first wave
+// adds them when it filters the page one step later.
 //
-// Exact streaming Top-K per query, kept entirely in LDS: positions arrive in
-// increasing order; a position is appended to the query's candidate buffer
-// (key, position) if its key beats the running threshold.  When the buffer
-// nears capacity one wave compacts it to exactly the current top K (register
-// radix select, ties to the lower -- earlier -- position) and the threshold
-// becomes that K-th key, compared strictly from then on: a later position
-// with an equal key ranks behind every kept one.  The buffer therefore always
-// holds the top K of the positions seen so far plus later contenders, in
-// position order; a final compaction writes the indices.  Scores never leave
-// the chip.
+// Exact streaming Top-K per query, kept in LDS: positions arrive in
+// increasing order and a position is appended to the query's candidate
+// buffer (key, position) if its key reaches the running threshold tau.  An
+// append also counts the key in a 256-bin histogram over [tau, max key].
+// When the buffer nears capacity the histogram alone gives a new tau -- the
+// lower edge of the bin holding the K-th largest key, so at least K seen keys
+// stay above it -- and one in-order pass drops the keys below it.  Only when
+// that frees too little (the first fill, heavy ties) does the wave run an
+// exact radix selection, which keeps exactly the top K (ties to the lower,
+// earlier, position) and makes tau strict: a later position with an equal
+// key ranks behind every kept one.  The buffer therefore always holds the top
+// K of the positions seen so far plus later contenders, in position order; a
+// final exact selection writes the indices.  Scores never leave the chip.
 #include "device_common.h"
 #include "launch.h"
 
@@ -35,45 +42,50 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
 
 constexpr int kPfQueries = 4;             // queries per workgroup
-constexpr int kPfWaves = 2 * kPfQueries;  // one wave per (query, head half)
+constexpr int kPfWaves = 2 * kPfQueries;  // one wave per (query, position half)
 constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfTile = 64;               // positions per key tile = one page
+constexpr int kPfRing = 3;                // key tiles: one read, one landed, one in flight
 constexpr int kPfCap = 3072;              // candidate slots per query
-constexpr int kPfRing = 3;                // key tiles in flight + in use
+constexpr int kPfRoom = 640;              // a threshold-only compaction must leave this many free
 
 struct PfSmem {
-  alignas(16) unsigned char ring[kPfRing][8192];  // 32 positions x 256 bytes
-  uint32_t key[kPfQueries][kPfCap];
-  int32_t pos[kPfQueries][kPfCap];
-  float xsum[2][kPfQueries][2][32];  // per-head-half partial scores of a tile
-  alignas(16) float w[kPfQueries][64];
+  alignas(16) unsigned char ring[kPfRing][kPfTile * 256];
+  uint64_t buf[kPfQueries][kPfCap];         // key | position << 32, position order
+  float xs[2][kPfQueries][2][kPfTile];      // [tile parity][query][lane half][position]
   uint32_t hist[kPfQueries][256];
-  int count[kPfQueries];
-  uint32_t tau[kPfQueries];
-  int strict[kPfQueries];
-  int pages[kMaxPrefillPages];
 };
 
-// LDS byte offset of (row, 16-byte chunk) inside a 32 x 256-byte key tile
-// written by 8 direct-to-LDS loads of one kilobyte each (four rows per load,
-// chunk position XOR-swizzled by row & 7).
-__device__ __forceinline__ int pf_slot(int row, int col) {
-  return 1024 * (row >> 2) + 16 * (16 * (row & 3) + 8 * (col >> 3) + ((col & 7) ^ (row & 7)));
+// LDS byte offset of (row, 16-byte chunk) in a 64 x 256-byte key tile: rows
+// are contiguous, chunks XOR-swizzled by row & 15, so 16 lanes reading the
+// same chunk of 16 consecutive rows hit 16 distinct bank groups.
+__device__ __forceinline__ int pf_slot(int row, int col) { return 256 * row + 16 * (col ^ (row & 15)); }
+
+// LDS atomic add written as the instruction itself: the compiler's wait
+// insertion cannot tell an atomic apart from the key-ring DMA and would drain
+// every tile load in flight before it.  LDS operations of a wave complete in
+// order, so later reads of the same wave see the sum; other waves read the
+// histogram only after an lgkmcnt(0) wait and a barrier.
+__device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
+  const uint32_t off = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)p;
+  asm volatile("ds_add_u32 %0, %1" ::"v"(off), "v"(v) : "memory");
 }
 
-// Wave-level exact selection over the query's buffer: finds the k-th largest
-// key (ties to the lower index), keeps exactly min(k, n) entries in order and
-// returns the new count; tau = the k-th key when n > k.
-__device__ int pf_compact(uint32_t* key, int32_t* pos, int n, int k, uint32_t* hist, uint32_t& tau, bool& cut) {
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Wave-level exact selection over buf[0..n), n > k >= 1: tau = the k-th
+// largest key, ties = how many entries equal to tau rank within the top k
+// (the earliest ones, buf being in position order).  hist is 256 words of
+// scratch.
+__device__ void pf_select(const uint64_t* buf, int n, int k, uint32_t* hist, uint32_t& tau, uint32_t& ties) {
   const int lane = threadIdx.x & (kWave - 1);
-  if (n <= k) {
-    cut = false;
-    return n;
-  }
-  // --- radix select of the k-th largest key over key[0..n) (wave-local)
   uint32_t lo = 0xffffffffu, hi = 0u;
   for (int i = lane; i < n; i += kWave) {
-    lo = min(lo, key[i]);
-    hi = max(hi, key[i]);
+    const uint32_t v = (uint32_t)buf[i];
+    lo = min(lo, v);
+    hi = max(hi, v);
   }
   lo = wave_min(lo);
   hi = wave_max(hi);
@@ -87,11 +99,21 @@ __device__ int pf_compact(uint32_t* key, int32_t* pos, int n, int k, uint32_t* h
       const int shift = top >= 7 ? top - 7 : 0;
       const int width = top - shift + 1;
       const uint32_t above = top == 31 ? 0u : ~((2u << top) - 1u);
-      for (int i = lane; i < 256; i += kWave) hist[i] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
       __builtin_amdgcn_s_waitcnt(0xC07F);
-      for (int i = lane; i < n; i += kWave) {
-        const uint32_t v = key[i];
-        if ((v & above) == prefix) atomicAdd(&hist[(v >> shift) & ((1u << width) - 1u)], 1u);
+      for (int base = 0; base < n; base += 4 * kWave) {
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = base + u * kWave + lane;
+          v[u] = i < n ? (uint32_t)buf[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = base + u * kWave + lane;
+          if (i < n && (v[u] & above) == prefix) atomicAdd(&hist[(v[u] >> shift) & ((1u << width) - 1u)], 1u);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);
       uint32_t h[4];
@@ -100,8 +122,9 @@ __device__ int pf_compact(uint32_t* key, int32_t* pos, int n, int k, uint32_t* h
       const uint32_t sum = h[0] + h[1] + h[2] + h[3];
       const uint32_t incl = wave_incl_scan(sum);
       const uint32_t excl = incl - sum;
+      const bool mine = excl < remaining && remaining <= incl;
       uint32_t dsel = 0, rsel = 0;
-      if (excl < remaining && remaining <= incl) {
+      if (mine) {
         uint32_t acc = excl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -112,9 +135,7 @@ __device__ int pf_compact(uint32_t* key, int32_t* pos, int n, int k, uint32_t* h
           acc += h[i];
         }
       }
-      // exactly one lane found the digit
-      const uint64_t who = __ballot(excl < remaining && remaining <= incl);
-      const int src = __ffsll((unsigned long long)who) - 1;
+      const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;  // exactly one lane
       dsel = __shfl(dsel, src, kWave);
       rsel = __shfl(rsel, src, kWave);
       prefix |= dsel << shift;
@@ -123,35 +144,41 @@ __device__ int pf_compact(uint32_t* key, int32_t* pos, int n, int k, uint32_t* h
     }
   }
   tau = prefix;
-  const uint32_t ties = remaining;  // entries equal to tau that stay (the earliest ones)
-  // --- in-order compaction to the front
+  ties = remaining;
+}
+
+// In-order compaction of buf[0..n): keeps keys > thr, and of the keys equal
+// to thr all of them (eq_all) or the first `ties`.  With `rebuild`, counts
+// every kept key into hist (already zero) over bins of width 2^hsh from
+// hbase, the last bin open-ended.  Returns the new count.
+__device__ int pf_compact_pass(uint64_t* buf, int n, uint32_t thr, bool eq_all, uint32_t ties, uint32_t* hist,
+                               uint32_t hbase, int hsh, bool rebuild) {
+  const int lane = threadIdx.x & (kWave - 1);
   int out = 0;
   uint32_t ties_seen = 0;
-  for (int base = 0; base < n; base += kWave) {
-    const int i = base + lane;
-    uint32_t v = 0;
-    int p = 0;
-    if (i < n) {
-      v = key[i];
-      p = pos[i];
+  for (int base = 0; base < n; base += 4 * kWave) {
+    uint64_t e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kWave + lane;
+      e[u] = i < n ? buf[i] : 0ull;
     }
-    const bool tie = i < n && v == tau;
-    const uint64_t tie_mask = __ballot(tie);
-    const uint32_t tie_rank = ties_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(tie_mask >> 32),
-                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)tie_mask, 0u));
-    const bool keep = i < n && (v > tau || (tie && tie_rank < ties));
-    const uint64_t keep_mask = __ballot(keep);
-    const int slot = out + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(keep_mask >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)keep_mask, 0u));
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // every lane has read its entry before any write
-    if (keep) {
-      key[slot] = v;
-      pos[slot] = p;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = base + u * kWave + lane < n;
+      const uint32_t key = (uint32_t)e[u];
+      const bool eq = valid && key == thr;
+      const uint64_t tie_mask = __ballot(eq);
+      const bool keep = valid && (key > thr || (eq && (eq_all || ties_seen + (uint32_t)lane_rank(tie_mask) < ties)));
+      const uint64_t keep_mask = __ballot(keep);
+      if (keep) {
+        buf[out + lane_rank(keep_mask)] = e[u];  // slot <= read index: never ahead of the reads
+        if (rebuild) atomicAdd(&hist[min(255u, (key - hbase) >> hsh)], 1u);
+      }
+      out += __popcll(keep_mask);
+      ties_seen += (uint32_t)__popcll(tie_mask);
     }
-    out += __popcll(keep_mask);
-    ties_seen += (uint32_t)__popcll(tie_mask);
   }
-  cut = true;
   return out;
 }
 
@@ -159,7 +186,7 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
   __shared__ PfSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qw = wid >> 1, part = wid & 1;  // query of this wave, head half
+  const int qw = wid & (kPfQueries - 1), ph = wid / kPfQueries;  // query of this wave, position half
   const int n = lane & 31, half = lane >> 5;
 
   // heaviest query blocks first
@@ -167,121 +194,216 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
   const int item = gridDim.x - 1 - blockIdx.x;
   const int b = item / nqb, qb = item % nqb;
   int L = a.seq_lens[b];
-  L = max(0, min(L, a.max_pages * 64));
+  L = max(0, min(L, a.max_pages * kPfTile));
   const int j0 = qb * kPfQueries;
   const int nq_here = min(kPfQueries, a.n_q - j0);
   const int* bt = a.block_table + (size_t)b * a.max_pages;
   // visible positions of each query of the block; the block streams the largest
   const int vis_last = max(0, min(L, L - a.n_q + j0 + nq_here));
-  const int n_tiles = (vis_last + 31) / 32;
-  const int n_pages = (vis_last + 63) / 64;
-
-  for (int i = tid; i < n_pages; i += kPfThreads) sm.pages[i] = min(max(bt[i], 0), a.num_pages - 1);
-  for (int i = tid; i < kPfQueries * 64; i += kPfThreads) {
-    const int qi = i / 64;
-    sm.w[qi][i % 64] = qi < nq_here ? a.w[((size_t)b * a.n_q + j0 + qi) * 64 + i % 64] : 0.f;
-  }
-  if (tid < kPfQueries) {
-    sm.count[tid] = 0;
-    sm.tau[tid] = 0u;
-    sm.strict[tid] = 0;
-  }
+  const int n_tiles = (vis_last + kPfTile - 1) / kPfTile;
   const bool q_ok = qw < nq_here;
   const int vis_q = q_ok ? max(0, min(L, L - a.n_q + j0 + qw + 1)) : 0;
+  const bool fin = ph == 0 && q_ok;  // this wave filters and selects for its query
 
-  // A operands: this wave's 32 heads of its query, k-step j = d 64*half+8j .. +8
-  bf16x8 qa[8];
+  // A operands: heads 32*blk + n of this wave's query; k-step j = d 64*half+8j .. +8.
+  // Head weights of the accumulator rows this lane holds: 32*blk + 8*(v/4) + 4*half + v%4.
+  bf16x8 qa[2][8];
+  float wv[2][16];
   {
-    const size_t row = ((size_t)b * a.n_q + j0 + (q_ok ? qw : 0)) * 64 + 32 * part + n;
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + row * 128 + 64 * half);
+    const size_t tok = (size_t)b * a.n_q + j0 + (q_ok ? qw : 0);
     const __bf16 keep = q_ok ? (__bf16)1.f : (__bf16)0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qa[j] = qp[j] * keep;
-  }
-  __syncthreads();
-
-  // direct-to-LDS load of tile t: wave w copies rows 4w..4w+3 (one kilobyte)
-  const int dma_row = 4 * wid + (lane >> 4);
-  const int dma_col = 8 * ((lane >> 3) & 1) + ((lane & 7) ^ (dma_row & 7));
-  auto issue = [&](int t) {
-    const int p0 = min(32 * t, max(vis_last - 1, 0));
-    const size_t rowi = (size_t)sm.pages[p0 >> 6] * 64 + (p0 & 32) + dma_row;
-    const char* src = static_cast<const char*>(a.k) + rowi * 256 + 16 * dma_col;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(sm.ring[t % kPfRing] + 1024 * wid), 16, 0, 0);
-  };
-
-  // the first wave of each query finalises scores of a tile and appends
-  auto finish_tile = [&](int t) {
-    if (part != 0 || !q_ok) return;
-    const float s = sm.xsum[t & 1][qw][0][n] + sm.xsum[t & 1][qw][1][n];
-    const int p = 32 * t + n;
-    const uint32_t k = score_key(s);
-    const uint32_t tau = sm.tau[qw];
-    const bool strict = sm.strict[qw] != 0;
-    const bool take = half == 0 && p < vis_q && (strict ? k > tau : k >= tau);
-    const uint64_t m = __ballot(take);
-    const int c = sm.count[qw];
-    if (take) {
-      const int slot = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      sm.key[qw][slot] = k;
-      sm.pos[qw][slot] = p;
-    }
-    int cnt = c + __popcll(m);
-    if (cnt > kPfCap - 32) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      uint32_t nt;
-      bool cut;
-      cnt = pf_compact(sm.key[qw], sm.pos[qw], cnt, a.top_k, sm.hist[qw], nt, cut);
-      if (cut && lane == 0) {
-        sm.tau[qw] = nt;
-        sm.strict[qw] = 1;
+    for (int blk = 0; blk < 2; ++blk) {
+      const bf16x8* qp =
+          reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + (tok * 64 + 32 * blk + n) * 128 + 64 * half);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qa[blk][j] = qp[j] * keep;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(a.w + tok * 64 + 32 * blk + 8 * g + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[blk][4 * g + i] = w4[i];
       }
     }
-    if (lane == 0) sm.count[qw] = cnt;
+  }
+  if (fin) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.hist[qw][4 * lane + i] = 0;
+  }
+  SLI_WAIT_VMCNT(0);  // register operands are in before the DMA accounting starts
+
+  // direct-to-LDS load of tile t: wave w copies rows 4i..4i+3 for i = w, w+8.
+  // The block table is read through the constant address space, so the
+  // wave-uniform page id comes from a scalar load and leaves the vector
+  // memory counter to the tile loads alone.
+  typedef __attribute__((address_space(4))) const int const_int;
+  const_int* btc = (const_int*)bt;
+  auto issue = [&](int t) {
+    const int pg = min(max(btc[t], 0), a.num_pages - 1);
+    const char* src = static_cast<const char*>(a.k) + (size_t)pg * (kPfTile * 256);
+    unsigned char* dst = sm.ring[(uint32_t)t % kPfRing];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = wid + kPfWaves * h;
+      const int row = 4 * i + (lane >> 4);
+      const int col = (lane & 15) ^ (row & 15);
+      __builtin_amdgcn_global_load_lds(src + row * 256 + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
+    }
   };
 
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 1) issue(1);
-#pragma unroll 1
-  for (int t = 0; t < n_tiles; ++t) {
-    // tile t has landed for this wave (only tile t+1 may be in flight) and
-    // its LDS writes are done; a raw barrier (no fence: a fence would also
-    // wait for the prefetch) then makes both visible to every wave
-    if (t + 1 < n_tiles) SLI_WAIT_VMCNT(1);
+  // selection state of the query (meaningful in the filtering wave only)
+  int cnt = 0;
+  uint32_t tau = 0u, hbase = 0u, kmax = 0u;
+  int hsh = 24;  // bins of the top 8 key bits until the first compaction
+  bool strict = false;
+  uint64_t* qbuf = sm.buf[qw];
+  uint32_t* qhist = sm.hist[qw];
+
+  auto compact = [&]() {
+    const uint32_t K = (uint32_t)a.top_k;
+    // bin holding the K-th largest key, counting from the top bin
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = qhist[255 - 4 * lane - i];
+    const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t excl = incl - sum;
+    const bool mine = excl < K && K <= incl;
+    uint32_t bsel = 0, kept = 0;
+    if (mine) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (acc < K && K <= acc + h[i]) {
+          bsel = 255u - 4u * lane - i;
+          kept = acc + h[i];
+        }
+        acc += h[i];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;  // every key is binned: total = cnt > K
+    bsel = __shfl(bsel, src, kWave);
+    kept = __shfl(kept, src, kWave);
+    uint32_t thr, ties = 0;
+    bool eq_all;
+    if (bsel >= 1 && kept <= (uint32_t)(kPfCap - kPfRoom)) {
+      thr = hbase + (bsel << hsh);  // lower edge of that bin: >= K seen keys reach it
+      eq_all = true;
+      strict = false;
+    } else {
+      pf_select(qbuf, cnt, (int)K, qhist, thr, ties);
+      eq_all = false;
+      strict = true;
+    }
+    tau = thr;
+    hbase = thr;
+    const uint32_t range = kmax - thr;
+    hsh = range > 255u ? 24 - __clz(range) : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qhist[4 * lane + i] = 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    cnt = pf_compact_pass(qbuf, cnt, thr, eq_all, ties, qhist, hbase, hsh, true);
+  };
+
+  // filter tile u of this query (both lane halves' partial sums) and append
+  auto finish = [&](int u) {
+    const float s = sm.xs[u & 1][qw][0][lane] + sm.xs[u & 1][qw][1][lane];
+    const int p = kPfTile * u + lane;
+    const uint32_t key = score_key(s);
+    const bool take = p < vis_q && (strict ? key > tau : key >= tau);
+    const uint64_t m = __ballot(take);
+    if (m != 0) {
+      if (take) {  // (bounded indices into sm, one 64-bit store: the compiler sees these miss the key ring)
+        sm.buf[qw][min((uint32_t)(cnt + lane_rank(m)), (uint32_t)kPfCap - 1u)] = ((uint64_t)p << 32) | key;
+        lds_add(&sm.hist[qw][min(255u, (key - hbase) >> hsh)], 1u);
+      }
+      cnt += __popcll(m);
+      kmax = max(kmax, wave_max(take ? key : 0u));
+      if (cnt > kPfCap - kPfTile) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        compact();
+      }
+    }
+  };
+
+  // MFMAs of tile t: rows 32*ph + n of the tile, both head blocks
+  auto mfma_tile = [&](int t, f32x16 (&acc)[2]) {
+    const unsigned char* T = sm.ring[(uint32_t)t % kPfRing];
+    bf16x8 kb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kb[j] = *reinterpret_cast<const bf16x8*>(T + pf_slot(32 * ph + n, 8 * half + j));
+    acc[0] = (f32x16){};
+    acc[1] = (f32x16){};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][j], kb[j], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][j], kb[j], acc[1], 0, 0, 0);
+    }
+  };
+
+  // weighted ReLU sum over this lane's 32 heads of tile t
+  auto epilogue = [&](int t, const f32x16 (&acc)[2]) {
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v & 3] += wv[blk][v] * fmaxf(acc[blk][v], 0.f);
+    sm.xs[t & 1][qw][half][32 * ph + n] = (s[0] + s[1]) + (s[2] + s[3]);
+  };
+
+  // Step t: tile t has landed (tile t+1 may be in flight), then a raw barrier
+  // (no fence: a fence would also wait for the prefetch) makes it and the
+  // partial sums of tile t-1 visible to every wave; it also frees the ring
+  // slot read at t-1 for tile t+2.
+  auto sync_step = [&](int t) {
+    if (t + 1 < n_tiles) SLI_WAIT_VMCNT(2);
     else SLI_WAIT_VMCNT(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
-    if (t > 0) finish_tile(t - 1);
-    const unsigned char* T = sm.ring[t % kPfRing];
-    bf16x8 kb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kb[j] = *reinterpret_cast<const bf16x8*>(T + pf_slot(n, 8 * half + j));
-    f32x16 acc = (f32x16){};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], kb[j], acc, 0, 0, 0);
-    float ps = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 w4 = *reinterpret_cast<const f32x4*>(&sm.w[qw][32 * part + 8 * g + 4 * half]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps += w4[i] * fmaxf(acc[4 * g + i], 0.f);
-    }
-    ps += __shfl_xor(ps, 32, kWave);
-    if (half == 0) sm.xsum[t & 1][qw][part][n] = ps;
     if (t + 2 < n_tiles) issue(t + 2);
+    if (fin && t >= 2 && t - 2 < n_tiles) finish(t - 2);
+  };
+
+  if (n_tiles > 0) {
+    f32x16 accA[2], accB[2];  // tile t lives in accA for even t, accB for odd t
+    issue(0);
+    if (n_tiles > 1) issue(1);
+    sync_step(0);
+    mfma_tile(0, accA);
+    int t = 1;
+#pragma unroll 1
+    for (; t + 1 < n_tiles; t += 2) {
+      sync_step(t);
+      mfma_tile(t, accB);
+      epilogue(t - 1, accA);
+      sync_step(t + 1);
+      mfma_tile(t + 1, accA);
+      epilogue(t, accB);
+    }
+    if (t < n_tiles) {  // one odd tile left
+      sync_step(t);
+      mfma_tile(t, accB);
+      epilogue(t - 1, accA);
+      sync_step(t + 1);
+      epilogue(t, accB);
+    } else {
+      sync_step(t);
+      epilogue(t - 1, accA);
+    }
+    sync_step(n_tiles + 1);  // filters the last tile
   }
-  __syncthreads();
-  if (n_tiles > 0) finish_tile(n_tiles - 1);
 
   // final selection and output (ascending positions, -1 padded)
-  if (part == 0 && q_ok) {
-    uint32_t nt;
-    bool cut;
-    int cnt = sm.count[qw];
-    cnt = pf_compact(sm.key[qw], sm.pos[qw], cnt, a.top_k, sm.hist[qw], nt, cut);
+  if (fin) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (cnt > a.top_k) {
+      uint32_t thr, ties;
+      pf_select(qbuf, cnt, a.top_k, qhist, thr, ties);
+      cnt = pf_compact_pass(qbuf, cnt, thr, false, ties, qhist, 0u, 0, false);
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     int32_t* out = a.idx_out + ((size_t)b * a.n_q + j0 + qw) * a.top_k;
-    for (int i = lane; i < a.top_k; i += kWave) out[i] = i < cnt ? sm.pos[qw][i] : -1;
+    for (int i = lane; i < a.top_k; i += kWave) out[i] = i < cnt ? (int32_t)(qbuf[i] >> 32) : -1;
   }
 }
 

@@ -31,7 +31,6 @@ struct IdxDecodeArgs {
   uint32_t* cand_cnt;  // [T][n_chunks_max]
 };
 
-constexpr int kMaxPrefillPages = 4096;  // prefill: positions per request <= 4096 pages
 
 struct IdxPrefillArgs {
   int B, n_q, max_pages, num_pages, top_k;

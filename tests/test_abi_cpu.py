@@ -41,7 +41,7 @@ def _call_topk(**over):
     (dict(q_dtype=1, k_dtype=1), -1), (dict(q_scales=ctypes.c_void_p(0x10000)), -1),
     (dict(q_per_seq=3, q_dtype=1, k_dtype=1, q_scales=ctypes.c_void_p(0x10000),
           k_scales=ctypes.c_void_p(0x10000)), -2),
-    (dict(q_per_seq=3, max_pages=5000), -2), (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(max_pages=10 ** 6), -2),
+    (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(max_pages=10 ** 6), -2),
     (dict(q=ctypes.c_void_p(0x10004)), -1),
 ])
 def test_score_topk_argument_errors(over, status):
