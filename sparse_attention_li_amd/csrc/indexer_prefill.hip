@@ -71,6 +71,10 @@ __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
   asm volatile("ds_add_u32 %0, %1" ::"v"(off), "v"(v) : "memory");
 }
 
+// max(x, 0) as one integer max on the bits: a negative float (or -0) is a
+// negative integer.  fmaxf would add a NaN-quieting canonicalisation.
+__device__ __forceinline__ float relu(float x) { return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0)); }
+
 __device__ __forceinline__ int lane_rank(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -232,28 +236,36 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
   }
   SLI_WAIT_VMCNT(0);  // register operands are in before the DMA accounting starts
 
-  // direct-to-LDS load of tile t: wave w copies rows 4i..4i+3 for i = w, w+8.
-  // The block table is read through the constant address space, so the
-  // wave-uniform page id comes from a scalar load and leaves the vector
-  // memory counter to the tile loads alone.
+  // Direct-to-LDS load of tile t: wave w copies rows 4i..4i+3 for i = w, w+8,
+  // through a buffer resource spanning exactly the tile's page (the hardware
+  // returns zeros for any offset outside it).  The block table is read
+  // through the constant address space, so the wave-uniform page id comes
+  // from a scalar load and leaves the vector memory counter to the tiles.
   typedef __attribute__((address_space(4))) const int const_int;
   const_int* btc = (const_int*)bt;
-  auto issue = [&](int t) {
-    const int pg = min(max(btc[t], 0), a.num_pages - 1);
-    const char* src = static_cast<const char*>(a.k) + (size_t)pg * (kPfTile * 256);
+  auto page = [&](int t) { return min(max(btc[min(t, n_tiles - 1)], 0), a.num_pages - 1); };
+  uint32_t dma_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 4 * (wid + kPfWaves * h) + (lane >> 4);
+    dma_off[h] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (row & 15)));
+  }
+  auto issue = [&](int t, int pg) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(a.k)) + (size_t)pg * (kPfTile * 256), (short)0, kPfTile * 256, 0x00020000);
     unsigned char* dst = sm.ring[(uint32_t)t % kPfRing];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = wid + kPfWaves * h;
-      const int row = 4 * i + (lane >> 4);
-      const int col = (lane & 15) ^ (row & 15);
-      __builtin_amdgcn_global_load_lds(src + row * 256 + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
-    }
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * (wid + kPfWaves * h)), 16, dma_off[h], 0, 0, 0);
   };
+  // B operands: row 32*ph + n of the tile, chunk 8*half + j for k-step j
+  uint32_t kb_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kb_off[j] = (uint32_t)pf_slot(32 * ph + n, 8 * half + j);
 
   // selection state of the query (meaningful in the filtering wave only)
   int cnt = 0;
-  uint32_t tau = 0u, hbase = 0u, kmax = 0u;
+  uint32_t tau = 0u, hbase = 0u;
   int hsh = 24;  // bins of the top 8 key bits until the first compaction
   bool strict = false;
   uint64_t* qbuf = sm.buf[qw];
@@ -297,7 +309,9 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
     }
     tau = thr;
     hbase = thr;
-    const uint32_t range = kmax - thr;
+    uint32_t kmax = 0u;
+    for (int i = lane; i < cnt; i += kWave) kmax = max(kmax, (uint32_t)qbuf[i]);
+    const uint32_t range = wave_max(kmax) - thr;
     hsh = range > 255u ? 24 - __clz(range) : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) qhist[4 * lane + i] = 0;
@@ -307,9 +321,9 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
 
   // filter tile u of this query (both lane halves' partial sums) and append
   auto finish = [&](int u) {
-    const float s = sm.xs[u & 1][qw][0][lane] + sm.xs[u & 1][qw][1][lane];
+    const float sc = sm.xs[u & 1][qw][0][lane] + sm.xs[u & 1][qw][1][lane];
     const int p = kPfTile * u + lane;
-    const uint32_t key = score_key(s);
+    const uint32_t key = score_key(sc);
     const bool take = p < vis_q && (strict ? key > tau : key >= tau);
     const uint64_t m = __ballot(take);
     if (m != 0) {
@@ -318,79 +332,90 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
         lds_add(&sm.hist[qw][min(255u, (key - hbase) >> hsh)], 1u);
       }
       cnt += __popcll(m);
-      kmax = max(kmax, wave_max(take ? key : 0u));
-      if (cnt > kPfCap - kPfTile) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        compact();
-      }
     }
   };
 
-  // MFMAs of tile t: rows 32*ph + n of the tile, both head blocks
-  auto mfma_tile = [&](int t, f32x16 (&acc)[2]) {
-    const unsigned char* T = sm.ring[(uint32_t)t % kPfRing];
-    bf16x8 kb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kb[j] = *reinterpret_cast<const bf16x8*>(T + pf_slot(32 * ph + n, 8 * half + j));
-    acc[0] = (f32x16){};
-    acc[1] = (f32x16){};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][j], kb[j], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][j], kb[j], acc[1], 0, 0, 0);
-    }
-  };
+  int pg_next = 0;   // page of the next tile to load
+  float part0 = 0.f; // head-block-0 partial sum of the previous tile (this lane's heads, position 32*ph + n)
+  f32x16 acc0, acc1; // head blocks 0 and 1 of the tile being multiplied
 
-  // weighted ReLU sum over this lane's 32 heads of tile t
-  auto epilogue = [&](int t, const f32x16 (&acc)[2]) {
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v & 3] += wv[blk][v] * fmaxf(acc[blk][v], 0.f);
-    sm.xs[t & 1][qw][half][32 * ph + n] = (s[0] + s[1]) + (s[2] + s[3]);
-  };
-
-  // Step t: tile t has landed (tile t+1 may be in flight), then a raw barrier
-  // (no fence: a fence would also wait for the prefetch) makes it and the
-  // partial sums of tile t-1 visible to every wave; it also frees the ring
-  // slot read at t-1 for tile t+2.
-  auto sync_step = [&](int t) {
-    if (t + 1 < n_tiles) SLI_WAIT_VMCNT(2);
+  // Step t (tile t's B operands are already in registers): wait until tile
+  // t+1 has landed (tile t+2 may be in flight); a raw barrier (no fence: it
+  // would also wait for the prefetch) makes it and the partial sums of tile
+  // t-1 visible to every wave and frees the slot of tile t, read during step
+  // t-1, for tile t+3.  Then
+  //   phase A: MFMA chain of head block 0 of tile t, with the head-block-1
+  //            weighted ReLU sum of tile t-1 (its partial goes to LDS);
+  //   phase B: MFMA chain of head block 1 of tile t, with the LDS reads of
+  //            tile t+1 and the head-block-0 sum of tile t.
+  // Each k-step's MFMA is followed by a small share of vector work that the
+  // wave issues while the MFMA runs; the scheduling fences keep it there.
+  // The query's first wave filters tile t-2 (both partials visible now).
+  auto step = [&](int t, const bf16x8 (&kc)[8], bf16x8 (&kn)[8], bool steady) {
+    if (steady || t + 2 < n_tiles) SLI_WAIT_VMCNT(2);
     else SLI_WAIT_VMCNT(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
-    if (t + 2 < n_tiles) issue(t + 2);
-    if (fin && t >= 2 && t - 2 < n_tiles) finish(t - 2);
+    if (steady || t + 3 < n_tiles) issue(t + 3, pg_next);
+    const bool cur = steady || t < n_tiles;
+    const bool prev = steady || (t >= 1 && t - 1 < n_tiles);
+    const bool next = steady || t + 1 < n_tiles;
+    if (fin && (steady || (t >= 2 && t - 2 < n_tiles))) finish(t - 2);
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (cur) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][j], kc[j], j ? acc0 : (f32x16){}, 0, 0, 0);
+      if (prev) {
+#pragma unroll
+        for (int v = 2 * j; v < 2 * j + 2; ++v) s[v & 3] += wv[1][v] * relu(acc1[v]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (prev) sm.xs[(t - 1) & 1][qw][half][32 * ph + n] = part0 + ((s[0] + s[1]) + (s[2] + s[3]));
+    float s0[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (cur) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][j], kc[j], j ? acc1 : (f32x16){}, 0, 0, 0);
+      if (next) kn[j] = *reinterpret_cast<const bf16x8*>(sm.ring[(uint32_t)(t + 1) % kPfRing] + kb_off[j]);
+      if (cur) {
+#pragma unroll
+        for (int v = 2 * j; v < 2 * j + 2; ++v) s0[v & 3] += wv[0][v] * relu(acc0[v]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    part0 = (s0[0] + s0[1]) + (s0[2] + s0[3]);
+    pg_next = page(t + 4);  // scalar load, used one step later
+    if (fin && cnt > kPfCap - kPfTile) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      compact();
+    }
   };
 
   if (n_tiles > 0) {
-    f32x16 accA[2], accB[2];  // tile t lives in accA for even t, accB for odd t
-    issue(0);
-    if (n_tiles > 1) issue(1);
-    sync_step(0);
-    mfma_tile(0, accA);
-    int t = 1;
+    bf16x8 kbA[8], kbB[8];  // B operands of tile t: kbA for even t, kbB for odd t
+    for (int i = 0; i < 3 && i < n_tiles; ++i) issue(i, page(i));
+    pg_next = page(3);
+    // tile 0 landed (tiles 1 and 2 may be in flight)
+    if (n_tiles > 2) SLI_WAIT_VMCNT(4);
+    else if (n_tiles > 1) SLI_WAIT_VMCNT(2);
+    else SLI_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kbA[j] = *reinterpret_cast<const bf16x8*>(sm.ring[0] + kb_off[j]);
+    step(0, kbA, kbB, false);
+    step(1, kbB, kbA, false);
+    int t = 2;
 #pragma unroll 1
-    for (; t + 1 < n_tiles; t += 2) {
-      sync_step(t);
-      mfma_tile(t, accB);
-      epilogue(t - 1, accA);
-      sync_step(t + 1);
-      mfma_tile(t + 1, accA);
-      epilogue(t, accB);
+    for (; t + 4 < n_tiles; t += 2) {
+      step(t, kbA, kbB, true);
+      step(t + 1, kbB, kbA, true);
     }
-    if (t < n_tiles) {  // one odd tile left
-      sync_step(t);
-      mfma_tile(t, accB);
-      epilogue(t - 1, accA);
-      sync_step(t + 1);
-      epilogue(t, accB);
-    } else {
-      sync_step(t);
-      epilogue(t - 1, accA);
+#pragma unroll 1
+    for (; t < n_tiles + 2; t += 2) {
+      step(t, kbA, kbB, false);
+      if (t + 1 < n_tiles + 2) step(t + 1, kbB, kbA, false);
     }
-    sync_step(n_tiles + 1);  // filters the last tile
   }
 
   // final selection and output (ascending positions, -1 padded)
