@@ -46,7 +46,7 @@ constexpr int kPfWaves = 2 * kPfQueries;  // one wave per (query, position half)
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfTile = 64;               // positions per key tile = one page
 constexpr int kPfRing = 3;                // key tiles: one read, one landed, one in flight
-constexpr int kPfCap = 3072;              // candidate slots per query
+constexpr int kPfCap = 3328;              // candidate slots per query (fills the LDS)
 constexpr int kPfRoom = 640;              // a threshold-only compaction must leave this many free
 
 struct PfSmem {
@@ -152,11 +152,12 @@ __device__ void pf_select(const uint64_t* buf, int n, int k, uint32_t* hist, uin
 }
 
 // In-order compaction of buf[0..n): keeps keys > thr, and of the keys equal
-// to thr all of them (eq_all) or the first `ties`.  With `rebuild`, counts
+// to thr all of them (kEqAll) or the first `ties`.  With `rebuild`, counts
 // every kept key into hist (already zero) over bins of width 2^hsh from
 // hbase, the last bin open-ended.  Returns the new count.
-__device__ int pf_compact_pass(uint64_t* buf, int n, uint32_t thr, bool eq_all, uint32_t ties, uint32_t* hist,
-                               uint32_t hbase, int hsh, bool rebuild) {
+template <bool kEqAll>
+__device__ int pf_compact_pass(uint64_t* buf, int n, uint32_t thr, uint32_t ties, uint32_t* hist, uint32_t hbase,
+                               int hsh, bool rebuild) {
   const int lane = threadIdx.x & (kWave - 1);
   int out = 0;
   uint32_t ties_seen = 0;
@@ -171,16 +172,21 @@ __device__ int pf_compact_pass(uint64_t* buf, int n, uint32_t thr, bool eq_all, 
     for (int u = 0; u < 4; ++u) {
       const bool valid = base + u * kWave + lane < n;
       const uint32_t key = (uint32_t)e[u];
-      const bool eq = valid && key == thr;
-      const uint64_t tie_mask = __ballot(eq);
-      const bool keep = valid && (key > thr || (eq && (eq_all || ties_seen + (uint32_t)lane_rank(tie_mask) < ties)));
+      bool keep;
+      if (kEqAll) {
+        keep = valid && key >= thr;
+      } else {
+        const bool eq = valid && key == thr;
+        const uint64_t tie_mask = __ballot(eq);
+        keep = valid && (key > thr || (eq && ties_seen + (uint32_t)lane_rank(tie_mask) < ties));
+        ties_seen += (uint32_t)__popcll(tie_mask);
+      }
       const uint64_t keep_mask = __ballot(keep);
       if (keep) {
         buf[out + lane_rank(keep_mask)] = e[u];  // slot <= read index: never ahead of the reads
         if (rebuild) atomicAdd(&hist[min(255u, (key - hbase) >> hsh)], 1u);
       }
       out += __popcll(keep_mask);
-      ties_seen += (uint32_t)__popcll(tie_mask);
     }
   }
   return out;
@@ -271,17 +277,18 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
   uint64_t* qbuf = sm.buf[qw];
   uint32_t* qhist = sm.hist[qw];
 
-  auto compact = [&]() {
+  // Bin holding the K-th largest key, counting from the top bin (the buffer
+  // holds more than K keys, all binned), and how many keys lie in it or above.
+  auto kth_bin = [&](uint32_t (&h)[4], uint32_t& bsel, uint32_t& kept) {
     const uint32_t K = (uint32_t)a.top_k;
-    // bin holding the K-th largest key, counting from the top bin
-    uint32_t h[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) h[i] = qhist[255 - 4 * lane - i];
     const uint32_t sum = h[0] + h[1] + h[2] + h[3];
     const uint32_t incl = wave_incl_scan(sum);
     const uint32_t excl = incl - sum;
     const bool mine = excl < K && K <= incl;
-    uint32_t bsel = 0, kept = 0;
+    bsel = 0;
+    kept = 0;
     if (mine) {
       uint32_t acc = excl;
 #pragma unroll
@@ -293,9 +300,37 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
         acc += h[i];
       }
     }
-    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;  // every key is binned: total = cnt > K
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
     bsel = __shfl(bsel, src, kWave);
     kept = __shfl(kept, src, kWave);
+  };
+  // Between compactions the threshold follows the histogram: the lower edge
+  // of the K-th key's bin has at least K seen keys at or above it.  Keys
+  // below it stay in the buffer (and their bins) until the next compaction.
+  auto raise = [&]() {
+    uint32_t h[4], bsel, kept;
+    kth_bin(h, bsel, kept);
+    const uint32_t edge = hbase + (bsel << hsh);
+    if (edge > tau) {
+      tau = edge;
+      strict = false;
+    }
+  };
+
+  auto compact = [&]() {
+    const uint32_t K = (uint32_t)a.top_k;
+    uint32_t h[4], bsel, kept;
+    kth_bin(h, bsel, kept);
+    const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+    // highest non-empty bin bounds the largest key (unless it is the open top bin)
+    const int top_lane = __ffsll((unsigned long long)__ballot(sum != 0)) - 1;
+    uint32_t btop = 0;
+#pragma unroll
+    for (int i = 3; i >= 0; --i)
+      if (h[i] != 0) btop = 255u - 4u * lane - i;
+    btop = __shfl(btop, top_lane, kWave);
+    const uint32_t old_base = hbase;
+    const int old_sh = hsh;
     uint32_t thr, ties = 0;
     bool eq_all;
     if (bsel >= 1 && kept <= (uint32_t)(kPfCap - kPfRoom)) {
@@ -309,14 +344,21 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
     }
     tau = thr;
     hbase = thr;
-    uint32_t kmax = 0u;
-    for (int i = lane; i < cnt; i += kWave) kmax = max(kmax, (uint32_t)qbuf[i]);
-    const uint32_t range = wave_max(kmax) - thr;
+    uint32_t kmax;
+    if (btop < 255u) {
+      kmax = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)old_base + ((uint64_t)(btop + 1u) << old_sh) - 1u);
+    } else {
+      kmax = 0u;
+      for (int i = lane; i < cnt; i += kWave) kmax = max(kmax, (uint32_t)qbuf[i]);
+      kmax = wave_max(kmax);
+    }
+    const uint32_t range = kmax - thr;
     hsh = range > 255u ? 24 - __clz(range) : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) qhist[4 * lane + i] = 0;
     __builtin_amdgcn_s_waitcnt(0xC07F);
-    cnt = pf_compact_pass(qbuf, cnt, thr, eq_all, ties, qhist, hbase, hsh, true);
+    cnt = eq_all ? pf_compact_pass<true>(qbuf, cnt, thr, 0u, qhist, hbase, hsh, true)
+                 : pf_compact_pass<false>(qbuf, cnt, thr, ties, qhist, hbase, hsh, true);
   };
 
   // filter tile u of this query (both lane halves' partial sums) and append
@@ -388,6 +430,9 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
     if (fin && cnt > kPfCap - kPfTile) {
       __builtin_amdgcn_s_waitcnt(0xC07F);
       compact();
+    } else if (fin && (t & 7) == 7 && cnt > a.top_k) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      raise();
     }
   };
 
@@ -424,7 +469,7 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
     if (cnt > a.top_k) {
       uint32_t thr, ties;
       pf_select(qbuf, cnt, a.top_k, qhist, thr, ties);
-      cnt = pf_compact_pass(qbuf, cnt, thr, false, ties, qhist, 0u, 0, false);
+      cnt = pf_compact_pass<false>(qbuf, cnt, thr, ties, qhist, 0u, 0, false);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     int32_t* out = a.idx_out + ((size_t)b * a.n_q + j0 + qw) * a.top_k;
