@@ -110,20 +110,32 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
   const int* bt = a.block_table + (size_t)b * a.max_pages;
 
   // ---------------------------------------------------------------- rows of this slice
+  // Every index load is in flight at once, then every block-table load: two
+  // memory latencies for the whole slice rather than two per row batch.
   if (tid == 0) s_fallback = 0x7fffffff;
-  __syncthreads();
-  for (int i = tid; i < n_tiles * kTileRows; i += NT) {
-    int r = -1;
-    if (i < cnt) {
-      const int pos = a.idx[(size_t)t * a.top_k + i0 + i];
-      if (pos >= 0 && pos < L) {
-        int page = bt[pos >> 6];
-        page = min(max(page, 0), a.num_pages - 1);
-        r = page * 64 + (pos & 63);
-        atomicMin(&s_fallback, r);
+  constexpr int RPT = kMaxSplitRows / NT;
+  const int n_rows = n_tiles * kTileRows;
+  int pos_v[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int i = tid + r * NT;
+    pos_v[r] = i < cnt ? a.idx[(size_t)t * a.top_k + i0 + i] : -1;
+  }
+  int page_v[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) page_v[r] = (pos_v[r] >= 0 && pos_v[r] < L) ? bt[pos_v[r] >> 6] : -1;
+  __syncthreads();  // s_fallback initialised
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int i = tid + r * NT;
+    if (i < n_rows) {
+      int rr = -1;
+      if (pos_v[r] >= 0 && pos_v[r] < L) {
+        rr = min(max(page_v[r], 0), a.num_pages - 1) * 64 + (pos_v[r] & 63);
+        atomicMin(&s_fallback, rr);
       }
+      rows[i] = rr;
     }
-    rows[i] = r;
   }
 
   // ---------------------------------------------------------------- q^T operands
@@ -237,9 +249,15 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     bf16x8 av[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) av[k] = *reinterpret_cast<const bf16x8*>(T + tile_off(n, 2 * (KS * part + k) + half));
-    f32x16 s = (f32x16){};
+    // two independent accumulator chains (even and odd k-steps) halve the
+    // dependent MFMA latency of the logits
+    f32x16 s = (f32x16){}, s_odd = (f32x16){};
 #pragma unroll
-    for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s, 0, 0, 0);
+    for (int k = 0; k < KS; k += 2) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s, 0, 0, 0);
+      if (k + 1 < KS) s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k + 1], qb[k + 1], s_odd, 0, 0, 0);
+    }
+    s += s_odd;
     if constexpr (WPH > 1) {
       xbuf[wid][lane] = s;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the partial is in LDS
@@ -258,9 +276,12 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
       mt = fmaxf(mt, x);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    {
-      // branch-free online-softmax update (a data-dependent branch here makes
-      // the compiler move the accumulators between register files every tile)
+    // Online softmax with a lazy reference: the running reference m_run is
+    // raised (and the accumulators rescaled) only when some head's tile
+    // maximum exceeds it by more than 2^8; otherwise the weights exp2(x -
+    // m_run) stay below 256, harmless in fp32 sums and bf16 operands.  The
+    // decision is wave-uniform, so most tiles skip the rescale entirely.
+    if (__ballot(mt > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = exp2f(m_run - m_new);
       l_run *= alpha;
