@@ -110,31 +110,33 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
   const int* bt = a.block_table + (size_t)b * a.max_pages;
 
   // ---------------------------------------------------------------- rows of this slice
-  // Every index load is in flight at once, then every block-table load: two
-  // memory latencies for the whole slice rather than two per row batch.
+  // Each batch has all of its index loads in flight at once, then all of its
+  // block-table loads: two memory latencies per batch of 8 rows per thread.
   if (tid == 0) s_fallback = 0x7fffffff;
-  constexpr int RPT = kMaxSplitRows / NT;
+  constexpr int RPB = 8;
   const int n_rows = n_tiles * kTileRows;
-  int pos_v[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int i = tid + r * NT;
-    pos_v[r] = i < cnt ? a.idx[(size_t)t * a.top_k + i0 + i] : -1;
-  }
-  int page_v[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) page_v[r] = (pos_v[r] >= 0 && pos_v[r] < L) ? bt[pos_v[r] >> 6] : -1;
   __syncthreads();  // s_fallback initialised
+#pragma unroll 1
+  for (int i0b = 0; i0b < n_rows; i0b += RPB * NT) {
+    int pos_v[RPB], page_v[RPB];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int i = tid + r * NT;
-    if (i < n_rows) {
-      int rr = -1;
-      if (pos_v[r] >= 0 && pos_v[r] < L) {
-        rr = min(max(page_v[r], 0), a.num_pages - 1) * 64 + (pos_v[r] & 63);
-        atomicMin(&s_fallback, rr);
+    for (int r = 0; r < RPB; ++r) {
+      const int i = i0b + tid + r * NT;
+      pos_v[r] = i < cnt ? a.idx[(size_t)t * a.top_k + i0 + i] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < RPB; ++r) page_v[r] = (pos_v[r] >= 0 && pos_v[r] < L) ? bt[pos_v[r] >> 6] : -1;
+#pragma unroll
+    for (int r = 0; r < RPB; ++r) {
+      const int i = i0b + tid + r * NT;
+      if (i < n_rows) {
+        int rr = -1;
+        if (pos_v[r] >= 0 && pos_v[r] < L) {
+          rr = min(max(page_v[r], 0), a.num_pages - 1) * 64 + (pos_v[r] & 63);
+          atomicMin(&s_fallback, rr);
+        }
+        rows[i] = rr;
       }
-      rows[i] = rr;
     }
   }
 
@@ -249,15 +251,22 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     bf16x8 av[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) av[k] = *reinterpret_cast<const bf16x8*>(T + tile_off(n, 2 * (KS * part + k) + half));
-    // two independent accumulator chains (even and odd k-steps) halve the
-    // dependent MFMA latency of the logits
-    f32x16 s = (f32x16){}, s_odd = (f32x16){};
+    // bf16: two independent accumulator chains (even and odd k-steps) halve
+    // the dependent MFMA latency of the logits; the FP8 variant keeps one
+    // chain (its staging registers leave no room for the second)
+    f32x16 s = (f32x16){};
+    if constexpr (!FP8) {
+      f32x16 s_odd = (f32x16){};
 #pragma unroll
-    for (int k = 0; k < KS; k += 2) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s, 0, 0, 0);
-      if (k + 1 < KS) s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k + 1], qb[k + 1], s_odd, 0, 0, 0);
+      for (int k = 0; k < KS; k += 2) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s, 0, 0, 0);
+        if (k + 1 < KS) s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k + 1], qb[k + 1], s_odd, 0, 0, 0);
+      }
+      s += s_odd;
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s, 0, 0, 0);
     }
-    s += s_odd;
     if constexpr (WPH > 1) {
       xbuf[wid][lane] = s;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the partial is in LDS
@@ -267,11 +276,14 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     }
 
     // online softmax; this lane owns head n and positions 8(v/4) + 4 half + v%4
+    // valid positions of the tile as one wave-uniform mask (lanes 32..63
+    // repeat lanes 0..31)
+    const uint32_t vmask = (uint32_t)__ballot(rows[tile * kTileRows + n] >= 0);
     float mt = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int pos = 8 * (v >> 2) + 4 * half + (v & 3);
-      const float x = rows[tile * kTileRows + pos] >= 0 ? s[v] * sl2 : -INFINITY;
+      const float x = ((vmask >> pos) & 1u) ? s[v] * sl2 : -INFINITY;
       s[v] = x;
       mt = fmaxf(mt, x);
     }
@@ -281,7 +293,9 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     // maximum exceeds it by more than 2^8; otherwise the weights exp2(x -
     // m_run) stay below 256, harmless in fp32 sums and bf16 operands.  The
     // decision is wave-uniform, so most tiles skip the rescale entirely.
-    if (__ballot(mt > m_run + 8.f) != 0) {
+    // (The FP8 single-head-group variant keeps the branch-free update: its
+    // staging registers leave no room for the branch.)
+    if (FP8 && NHG == 1 ? true : __ballot(mt > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = exp2f(m_run - m_new);
       l_run *= alpha;
