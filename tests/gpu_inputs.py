@@ -13,7 +13,10 @@ def _t(a: np.ndarray, dev):
 
 
 class GpuCase:
-    def __init__(self, case, dev="cuda", attention=True):
+    def __init__(self, case, dev="cuda", attention=True, latent_requests=None):
+        """latent_requests: if given, only those requests' latent rows are
+        generated (the pool keeps its full size; other pages hold code 0 with
+        scale 1), for full-size launches whose checks sample a few requests."""
         self.case = case
         self.dev = dev
         self.seq_lens = _t(case.seq_lens.astype(np.int32), dev)
@@ -26,12 +29,27 @@ class GpuCase:
         self.k_pool = _t(kp, dev)
         self.k_scales = None if ks is None else _t(ks, dev)
         del kp, ks
-        if attention:
+        if attention and latent_requests is None:
             self.mla_q = _t(case.mla_q(), dev)
             lp, ls = case.latent_pool()
             self.kv_pool = _t(lp, dev)
             self.kv_scales = None if ls is None else _t(ls, dev)
             del lp, ls
+        elif attention:
+            self.mla_q = _t(case.mla_q(), dev)
+            NP, fp8 = case.num_pages, case.kv_fmt != "bf16"
+            self.kv_pool = torch.zeros((NP, 64, 576), dtype=torch.uint8 if fp8 else torch.int16, device=dev)
+            self.kv_scales = torch.ones((NP, 64, case.kv_groups), dtype=torch.float32, device=dev) if fp8 else None
+            bt = case.block_table()
+            flat = self.kv_pool.view(NP * 64, 576)
+            for b in latent_requests:
+                L = int(case.seq_lens[b])
+                rows, sc = case.latent_rows(b)
+                s = np.arange(L)
+                phys = torch.from_numpy((bt[b, s // 64].astype(np.int64) * 64 + s % 64)).to(dev)
+                flat[phys] = _t(rows.view(np.uint8) if fp8 else rows.view(np.int16), dev)
+                if fp8:
+                    self.kv_scales.view(NP * 64, case.kv_groups)[phys] = _t(sc, dev)
 
     def score_topk(self, lib, **kw):
         c = self.case

@@ -207,3 +207,36 @@ def test_prefill_4k_on_64k_sampled(li):
     ores = oracle.run_tokens(case, tokens)
     _check_indices(case, idx.cpu().numpy(), tokens, ores)
     _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
+
+
+def test_decode_b64_var_fp8_sampled(li):
+    """Full-size FP8 workload (64 requests of 4K..128K positions, MXFP8 indexer
+    query, FP8 keys and latent), same launches as a decode step; sampled
+    requests (shortest, longest, first, last) checked end to end.  Latent rows
+    are generated for the sampled requests only."""
+    case = synth.workload("decode_b64_var_fp8")
+    L = case.seq_lens
+    tokens = sorted({0, case.B - 1, int(np.argmin(L)), int(np.argmax(L))})
+    g = GpuCase(case, latent_requests=tokens)
+    idx = g.score_topk(li)
+    out, lse = g.attend(li, idx)
+    torch.cuda.synchronize()
+    ores = oracle.run_tokens(case, tokens)
+    _check_indices(case, idx.cpu().numpy(), tokens, ores)
+    _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
+
+
+def test_decode_b128_ctx128k_mtp2_sampled(li):
+    """Full-size two-token verification workload: 128 requests x 131072
+    positions, FP8 keys, latent FP8 with one scale per 128-wide tile; both
+    tokens of the first and last request checked end to end."""
+    case = synth.workload("decode_b128_ctx128k_mtp2")
+    reqs = [0, case.B - 1]
+    g = GpuCase(case, latent_requests=reqs)
+    idx = g.score_topk(li)
+    out, lse = g.attend(li, idx)
+    torch.cuda.synchronize()
+    tokens = [r * case.n_q + j for r in reqs for j in range(case.n_q)]
+    ores = oracle.run_tokens(case, tokens)
+    _check_indices(case, idx.cpu().numpy(), tokens, ores)
+    _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
