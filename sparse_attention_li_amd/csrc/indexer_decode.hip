@@ -64,7 +64,7 @@ struct IdxSmem {
   uint32_t hist[256];
   uint32_t cbase[kMaxChunksPerSeq + 1];
   uint32_t sel[2];
-  uint32_t scan[8];
+  uint32_t scan[16];
   uint32_t flag[4];
 };
 
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
   for (int i = tid; i < NQ * 64; i += kIdxThreads) sm.w[i / 64][i % 64] = a.w[(size_t)(t0 + i / 64) * 64 + i % 64];
   for (int i = tid; i < CHUNK / 64; i += kIdxThreads) {
     const int lp = s0 / 64 + i;
-    sm.pages[i] = lp * 64 < L ? min(max(bt[lp], 0), a.num_pages - 1) : 0;
+    const int pg = lp < a.max_pages ? bt[lp] : 0;  // in bounds whatever L is: no wait on seq_lens first
+    sm.pages[i] = lp * 64 < L ? min(max(pg, 0), a.num_pages - 1) : 0;
   }
   if constexpr (FP8) {
     __syncthreads();
@@ -376,6 +377,7 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
     if (tid == 0) sm.cbase[n_chunks] = N;
     __syncthreads();
     // flat candidate f -> (chunk, slot) by binary search over the prefix offsets
+    // (only for the out-of-LDS fallback)
     auto locate = [&](int f) {
       int lo = 0, hi = n_chunks;  // cbase[lo] <= f < cbase[hi]
       while (hi - lo > 1) {
@@ -386,28 +388,35 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
     };
     const bool in_lds = N <= (uint32_t)kCandCap;
     if (in_lds) {
-      // all addresses first, then all loads in flight at once
-      constexpr int PERT = kCandCap / kIdxThreads;
-      size_t gaddr[PERT];
+      // Chunk by chunk: thread i takes slot i (+256, ...) of each chunk's
+      // region, with the loads of 8 chunks in flight at once.
+      constexpr int GB = 8;
+#pragma unroll 1
+      for (int c0 = 0; c0 < n_chunks; c0 += GB) {
+        uint32_t maxc = 0;
+        for (int u = 0; u < GB && c0 + u < n_chunks; ++u) maxc = max(maxc, sm.cbase[c0 + u + 1] - sm.cbase[c0 + u]);
+#pragma unroll 1
+        for (uint32_t s0 = 0; s0 < maxc; s0 += kIdxThreads) {
+          uint32_t kv[GB];
+          int32_t pv[GB];
 #pragma unroll
-      for (int r = 0; r < PERT; ++r) {
-        const int f = tid + r * kIdxThreads;
-        gaddr[r] = f < (int)N ? locate(f) : 0;
-      }
-      uint32_t kv[PERT];
-      int32_t pv[PERT];
+          for (int u = 0; u < GB; ++u) {
+            const int cc2 = c0 + u;
+            const uint32_t sl = s0 + tid;
+            const bool ok = cc2 < n_chunks && sl < sm.cbase[min(cc2 + 1, n_chunks)] - sm.cbase[min(cc2, n_chunks)];
+            const size_t ga = (tok * ncm + cc2) * CHUNK + sl;
+            kv[u] = ok ? xload(&a.cand_key[ga]) : 0u;
+            pv[u] = ok ? xload(&a.cand_pos[ga]) : -1;
+          }
 #pragma unroll
-      for (int r = 0; r < PERT; ++r) {
-        const int f = tid + r * kIdxThreads;
-        kv[r] = f < (int)N ? xload(&a.cand_key[gaddr[r]]) : 0u;
-        pv[r] = f < (int)N ? xload(&a.cand_pos[gaddr[r]]) : -1;
-      }
-#pragma unroll
-      for (int r = 0; r < PERT; ++r) {
-        const int f = tid + r * kIdxThreads;
-        if (f < (int)N) {
-          s_ck[f] = kv[r];
-          s_cp[f] = pv[r];
+          for (int u = 0; u < GB; ++u) {
+            const int cc2 = c0 + u;
+            const uint32_t sl = s0 + tid;
+            if (cc2 < n_chunks && sl < sm.cbase[cc2 + 1] - sm.cbase[cc2]) {
+              s_ck[sm.cbase[cc2] + sl] = kv[u];
+              s_cp[sm.cbase[cc2] + sl] = pv[u];
+            }
+          }
         }
       }
       __syncthreads();
@@ -425,34 +434,78 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
       ties = K - ngt;
     }
     int32_t* out = a.idx_out + tok * K;
-    // Each thread walks a contiguous segment of the (position-ordered)
-    // candidates: one scan ranks the ties at tau, one places the selected.
-    const int seg = ((int)N + kIdxThreads - 1) / kIdxThreads;
-    const int f_lo = min((int)N, tid * seg), f_hi = min((int)N, f_lo + seg);
-    uint32_t my_ties = 0;
-    if (!take_all)
-      for (int f = f_lo; f < f_hi; ++f) my_ties += key_at(f) == tau ? 1u : 0u;
-    uint32_t tie_tot;
-    uint32_t tie_rank = block_excl_scan(my_ties, sm.scan, tie_tot);
-    uint32_t my_sel = 0;
-    {
-      uint32_t tr = tie_rank;
-      for (int f = f_lo; f < f_hi; ++f) {
-        const uint32_t key = key_at(f);
-        const bool tie = !take_all && key == tau;
-        my_sel += (take_all || key > tau || (tie && tr < (uint32_t)ties)) ? 1u : 0u;
-        tr += tie ? 1u : 0u;
-      }
-    }
     uint32_t written;
-    uint32_t o = block_excl_scan(my_sel, sm.scan, written);
-    {
-      uint32_t tr = tie_rank;
-      for (int f = f_lo; f < f_hi; ++f) {
-        const uint32_t key = key_at(f);
-        const bool tie = !take_all && key == tau;
-        if (take_all || key > tau || (tie && tr < (uint32_t)ties)) out[o++] = pos_at(f);
-        tr += tie ? 1u : 0u;
+    if (in_lds) {
+      // In position order, 256 candidates per round: wave ballots rank the
+      // ties at tau and then the selected candidates inside each wave, and
+      // per-wave counts (double-buffered by round parity) rank the waves.
+      const int wid_ = tid >> 6;
+      constexpr int NWV = kIdxThreads / kWave;
+      uint32_t base = 0, ties_before = 0;
+      for (int f0 = 0, rnd = 0; f0 < (int)N; f0 += kIdxThreads, ++rnd) {
+        const int f = f0 + tid;
+        const uint32_t key = f < (int)N ? s_ck[f] : 0u;
+        const bool gt = f < (int)N && (take_all || key > tau);
+        const bool tie = f < (int)N && !take_all && key == tau;
+        uint32_t* cnts = sm.scan + 8 * (rnd & 1);
+        const uint64_t mt = __ballot(tie);
+        if (lane == 0) cnts[wid_] = (uint32_t)__popcll(mt);
+        __syncthreads();
+        uint32_t tb = 0, tt = 0;
+        for (int w2 = 0; w2 < NWV; ++w2) {
+          const uint32_t x = cnts[w2];
+          tb += w2 < wid_ ? x : 0u;
+          tt += x;
+        }
+        const uint32_t tie_rank =
+            ties_before + tb + __builtin_amdgcn_mbcnt_hi((uint32_t)(mt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
+        const bool sel = gt || (tie && tie_rank < (uint32_t)ties);
+        const uint64_t m = __ballot(sel);
+        if (lane == 0) cnts[NWV + wid_] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t before = 0, tot = 0;
+        for (int w2 = 0; w2 < NWV; ++w2) {
+          const uint32_t x = cnts[NWV + w2];
+          before += w2 < wid_ ? x : 0u;
+          tot += x;
+        }
+        if (sel) {
+          const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          out[base + before + r] = s_cp[f];
+        }
+        base += tot;
+        ties_before += tt;
+      }
+      written = base;
+    } else {
+      // Each thread walks a contiguous segment of the (position-ordered)
+      // candidates: one scan ranks the ties at tau, one places the selected.
+      const int seg = ((int)N + kIdxThreads - 1) / kIdxThreads;
+      const int f_lo = min((int)N, tid * seg), f_hi = min((int)N, f_lo + seg);
+      uint32_t my_ties = 0;
+      if (!take_all)
+        for (int f = f_lo; f < f_hi; ++f) my_ties += key_at(f) == tau ? 1u : 0u;
+      uint32_t tie_tot;
+      uint32_t tie_rank = block_excl_scan(my_ties, sm.scan, tie_tot);
+      uint32_t my_sel = 0;
+      {
+        uint32_t tr = tie_rank;
+        for (int f = f_lo; f < f_hi; ++f) {
+          const uint32_t key = key_at(f);
+          const bool tie = !take_all && key == tau;
+          my_sel += (take_all || key > tau || (tie && tr < (uint32_t)ties)) ? 1u : 0u;
+          tr += tie ? 1u : 0u;
+        }
+      }
+      uint32_t o = block_excl_scan(my_sel, sm.scan, written);
+      {
+        uint32_t tr = tie_rank;
+        for (int f = f_lo; f < f_hi; ++f) {
+          const uint32_t key = key_at(f);
+          const bool tie = !take_all && key == tau;
+          if (take_all || key > tau || (tie && tr < (uint32_t)ties)) out[o++] = pos_at(f);
+          tr += tie ? 1u : 0u;
+        }
       }
     }
     for (int i = (int)written + tid; i < K; i += kIdxThreads) out[i] = -1;
