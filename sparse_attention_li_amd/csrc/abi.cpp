@@ -73,11 +73,13 @@ IdxLayout idx_layout(int B, int n_q, int max_pages) {
   return l;
 }
 
-// Splits of the index row so that about one workgroup per CU is busy (the
-// attention workgroup fills a CU: one wave per SIMD).
-void sfa_shape(int T, int H, int top_k, int& n_splits, int& split_len) {
+// Splits of the index row so that about one workgroup per CU is busy (an
+// attention workgroup fills a CU: one wave per SIMD).  bf16 workgroups hold
+// every head of a token; FP8 ones a block of up to 64 heads.
+void sfa_shape(int T, int H, int top_k, bool fp8, int& n_splits, int& split_len) {
   const int cus = device_cus();
-  const int head_blocks = (H + sli::sfa_heads_per_block(H) - 1) / sli::sfa_heads_per_block(H);
+  const int hpb = sli::sfa_heads_per_block(H, fp8);
+  const int head_blocks = (H + hpb - 1) / hpb;
   const int per_split = T * head_blocks;
   int s = std::max(1, (cus + per_split - 1) / per_split);
   s = std::min(s, std::max(1, top_k / 64));
@@ -85,6 +87,11 @@ void sfa_shape(int T, int H, int top_k, int& n_splits, int& split_len) {
   split_len = (split_len + 31) / 32 * 32;
   split_len = std::min(split_len, sli::kMaxSplitRows);
   n_splits = (top_k + split_len - 1) / split_len;
+}
+
+size_t sfa_partials_bytes(int T, int H, int n_splits) {
+  if (n_splits == 1) return 256;
+  return round_up((size_t)T * n_splits * H * 512 * 2, 256) + round_up((size_t)T * n_splits * H * 2 * 4, 256);
 }
 
 li_status check_paged(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
@@ -194,12 +201,13 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
 
 size_t sfa_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t top_k) {
   if (num_tokens <= 0 || num_heads <= 0 || top_k <= 0) return 0;
-  int s, len;
-  sfa_shape(num_tokens, num_heads, top_k, s, len);
-  if (s == 1) return 256;
-  size_t po = (size_t)num_tokens * s * num_heads * 512 * 4;
-  size_t pm = (size_t)num_tokens * s * num_heads * 2 * 4;
-  return round_up(po, 256) + round_up(pm, 256);
+  size_t need = 0;
+  for (bool fp8 : {false, true}) {
+    int s, len;
+    sfa_shape(num_tokens, num_heads, top_k, fp8, s, len);
+    need = std::max(need, sfa_partials_bytes(num_tokens, num_heads, s));
+  }
+  return need;
 }
 
 static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
@@ -227,7 +235,7 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
     return fail(LI_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
   const int T = num_seqs * q_per_seq;
   int s, len;
-  sfa_shape(T, num_heads, top_k, s, len);
+  sfa_shape(T, num_heads, top_k, fp8, s, len);
   sli::SfaArgs a;
   a.T = T;
   a.n_q = q_per_seq;
@@ -238,7 +246,7 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
   a.kv_groups = fp8 ? kv_scale_groups : 1;
   a.n_splits = s;
   a.split_len = len;
-  a.head_blocks = (num_heads + sli::sfa_heads_per_block(num_heads) - 1) / sli::sfa_heads_per_block(num_heads);
+  a.head_blocks = (num_heads + sli::sfa_heads_per_block(num_heads, fp8) - 1) / sli::sfa_heads_per_block(num_heads, fp8);
   a.sm_scale = sm_scale;
   a.seq_lens = seq_lens;
   a.block_table = block_table;
@@ -257,8 +265,8 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
       return fail(LI_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
     if (!aligned16(workspace)) return fail(LI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     char* ws = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(ws);
-    a.part_ml = reinterpret_cast<float*>(ws + round_up((size_t)T * s * num_heads * 512 * 4, 256));
+    a.part_o = reinterpret_cast<__bf16*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + round_up((size_t)T * s * num_heads * 512 * 2, 256));
   }
   hipError_t e = sli::launch_sfa(a, fp8, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LI_OK : hip_fail(e, "attention launch");

@@ -54,8 +54,8 @@ struct SfaArgs {
   const int32_t* idx;
   void* out;
   float* lse;
-  float* part_o;   // [T][n_splits][H][512]
-  float* part_ml;  // [T][n_splits][H][2]
+  __bf16* part_o;  // [T][n_splits][H][512] split output normalised by its own sum
+  float* part_ml;  // [T][n_splits][H][2]   (running max in log2 units, sum)
 };
 
 int idx_decode_chunk(int B, int n_q, int max_pages, int cus);
@@ -63,6 +63,6 @@ hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStr
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);
-int sfa_heads_per_block(int H);
+int sfa_heads_per_block(int H, bool fp8);
 
 }  // namespace sli
