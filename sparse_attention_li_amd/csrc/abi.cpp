@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.h"
@@ -46,31 +47,40 @@ int device_cus() {
 
 struct IdxLayout {
   int chunk, ncm;
-  size_t off_counters, off_samples, off_key, off_pos, off_cnt, total;
+  size_t off_counters, off_refs, off_cnts, off_cand, total;
 };
 
-IdxLayout idx_layout(int B, int n_q, int max_pages) {
+IdxLayout idx_layout(int B, int n_q, bool fp8, int max_pages) {
   IdxLayout l;
-  l.chunk = sli::idx_decode_chunk(B, n_q, max_pages, device_cus());
+  l.chunk = sli::idx_decode_chunk(B, n_q, fp8, max_pages, device_cus());
   const long long maxlen = (long long)max_pages * 64;
   l.ncm = (int)std::max<long long>(1, (maxlen + l.chunk - 1) / l.chunk);
   const size_t T = (size_t)B * n_q;
   size_t o = 0;
-  // The barrier counters sit in a fixed region at the start whatever the
+  // The exchange counters sit in a fixed region at the start whatever the
   // geometry, so a workspace reused for another batch shape never finds the
-  // previous call's samples or candidates where it expects zeroed counters.
+  // previous call's lists where it expects zeroed counters.
   l.off_counters = o;
   o = round_up(o + (size_t)sli::kMaxSeqs * sli::kCounterStride * 4, 256);
-  l.off_samples = o;
-  o = round_up(o + T * l.ncm * (l.chunk / sli::kSampleEvery) * 4, 256);
-  l.off_key = o;
-  o = round_up(o + T * l.ncm * l.chunk * 4, 256);
-  l.off_pos = o;
-  o = round_up(o + T * l.ncm * l.chunk * 4, 256);
-  l.off_cnt = o;
-  o = round_up(o + T * l.ncm * 4, 256);
+  l.off_refs = o;
+  o = round_up(o + T * l.ncm * 2 * 8, 256);
+  l.off_cnts = o;
+  o = round_up(o + T * l.ncm * 8, 256);
+  l.off_cand = o;
+  o = round_up(o + T * l.ncm * l.chunk * 8, 256);
   l.total = o;
   return l;
+}
+
+// Polls an exchange wait makes before giving up (a test hook can lower it
+// through LI_SPIN_MAX to exercise the fallbacks).
+int spin_max() {
+  const char* e = getenv("LI_SPIN_MAX");
+  if (e && *e) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 0 && v < (1L << 30)) return (int)v;
+  }
+  return 20000;
 }
 
 // Splits of the index row so that about one workgroup per CU is busy (an
@@ -116,7 +126,10 @@ const char* li_last_error(void) { return g_err; }
 size_t li_score_topk_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t top_k) {
   if (num_seqs <= 0 || q_per_seq <= 0 || max_pages <= 0 || top_k <= 0) return 0;
   if (q_per_seq > 2) return 256;  // the prefill kernel keeps its selection state in LDS
-  return idx_layout(num_seqs, q_per_seq, max_pages).total;
+  // (the layout depends on the chunk length, which differs between bf16 and
+  // FP8 for two-token calls: the larger of the two)
+  return std::max(idx_layout(num_seqs, q_per_seq, false, max_pages).total,
+                  idx_layout(num_seqs, q_per_seq, true, max_pages).total);
 }
 
 li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* stream) {
@@ -165,7 +178,7 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
     return e == hipSuccess ? LI_OK : hip_fail(e, "prefill indexer launch");
   }
   if (num_seqs > sli::kMaxSeqs) return fail(LI_ERR_UNSUPPORTED, "num_seqs %d exceeds %d", num_seqs, sli::kMaxSeqs);
-  const IdxLayout l = idx_layout(num_seqs, q_per_seq, max_pages);
+  const IdxLayout l = idx_layout(num_seqs, q_per_seq, fp8, max_pages);
   if (l.ncm > sli::kMaxChunksPerSeq)
     return fail(LI_ERR_UNSUPPORTED, "max_pages*64 = %lld positions exceeds %d", (long long)max_pages * 64,
                 sli::kMaxChunksPerSeq * l.chunk);
@@ -191,10 +204,10 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
   a.idx_out = idx_out;
   char* ws = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<uint32_t*>(ws + l.off_counters);
-  a.samples = reinterpret_cast<uint32_t*>(ws + l.off_samples);
-  a.cand_key = reinterpret_cast<uint32_t*>(ws + l.off_key);
-  a.cand_pos = reinterpret_cast<int32_t*>(ws + l.off_pos);
-  a.cand_cnt = reinterpret_cast<uint32_t*>(ws + l.off_cnt);
+  a.refs = reinterpret_cast<uint64_t*>(ws + l.off_refs);
+  a.cnts = reinterpret_cast<uint64_t*>(ws + l.off_cnts);
+  a.cand = reinterpret_cast<uint64_t*>(ws + l.off_cand);
+  a.spin_max = spin_max();
   hipError_t e = sli::launch_idx_decode(a, l.chunk, fp8, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LI_OK : hip_fail(e, "indexer launch");
 }

@@ -17,21 +17,25 @@
 // reduction sum_h w*ReLU(S) is 16 in-lane FMAs plus one cross-half swap.
 // Scores become order-preserving uint32 keys in LDS; they never reach HBM.
 //
-// Exact selection across workgroups without writing the scores out:
-//   1. each workgroup sorts a copy of its chunk's keys in LDS and publishes
-//      order statistics: the key at descending rank 32i-1 certifies that the
-//      chunk holds >= 32i keys >= it;
-//   2. after every chunk of the request has published (a bounded wait on an
-//      arrival counter), the m-th largest sample, m = ceil(K/32), is a lower
-//      bound tau on the K-th largest score of the request: the samples above
-//      it certify >= K keys >= tau;
-//   3. each workgroup appends only its keys >= tau (in position order) to its
-//      own candidate region -- about K + 32 per chunk in all, not the scores;
-//   4. the last workgroup to finish runs an exact radix select over the
-//      candidates and writes the indices in ascending position order.
-// If the wait times out (the request's chunks were not co-resident) the
-// workgroup falls back to tau = "every valid key", which keeps the result
-// exact and only costs candidate bytes.
+// Exact selection across the n chunks of a request, every workgroup writing
+// its own chunk's share of the output (kappa = the K-th largest key):
+//   1. with R = ceil(K/n), each chunk finds, from one LDS histogram of its
+//      keys, a key interval [lo_c, hi_c) holding its R-th largest key:
+//      >= R of its keys are >= lo_c and < R are >= hi_c.  Hence
+//      lo = min lo_c and hi = max hi_c bracket kappa: >= nR >= K keys are
+//      >= lo, and <= n(R-1) < K keys are >= hi.  Exchange 1 publishes the
+//      intervals;
+//   2. keys >= hi are selected for certain; each chunk publishes its count of
+//      them and its "band" keys in [lo, hi) with their positions (exchange 2);
+//   3. every workgroup loads all band keys of the request (a few per cent of
+//      the positions), selects kappa among them exactly (radix select,
+//      need = K - #keys >= hi), counts what the chunks before it select, and
+//      writes its own selected positions at that offset, in position order.
+// The exchanges are arrival counters with bounded waits.  A workgroup whose
+// first wait times out (its request's chunks were not all resident) publishes
+// every key as band, which keeps the result exact; one whose second wait
+// times out leaves its share to the last workgroup to arrive, which then
+// writes the whole request from the published lists.
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,32 +44,43 @@ namespace sli {
 typedef __attribute__((address_space(3))) void lds_void;
 #define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
 
-constexpr int kIdxThreads = 256;
-constexpr int kRun = 256;               // keys one wave sorts in registers
-constexpr int kCandCap = 4096;          // candidates the final select keeps in LDS
-constexpr unsigned kSpinMax = 20000;    // ~1 ms of s_sleep(2) before falling back
+constexpr int kHistBins = 4096;  // LDS histogram that brackets a chunk's R-th largest key
+constexpr int kBandCap = 4096;   // band entries the final select keeps in LDS
 
-constexpr int kSampleCap = 4096;        // samples of one request the bound search keeps in LDS
+// Per-request words of the fixed counter region (one 128-byte line each).
+// Exchange data carries a per-call tag (the request's epoch + 1) in its upper
+// 32 bits, so a reader polls the data itself: no counter, no fence on the
+// common path.  The counters only settle the rare give-up fallback and let
+// the last workgroup to leave reset the line and advance the epoch.
+enum : uint32_t { kArrive2 = 0, kDone = 1, kState = 2, kEpoch = 4 };
+enum : uint32_t { kStLast = 1u, kStGaveUp = 2u };
+enum : uint32_t { kModeNormal = 0u, kModeFull = 1u, kModeQuit = 2u };
 
 // LDS: a per-wave ring of two key tiles filled by direct-to-LDS loads during
-// scoring; after scoring the same bytes hold the request's samples (bound
-// search) and, in the last workgroup, the candidates of the final select.
-template <int NQ, int CHUNK, bool FP8>
+// scoring; after scoring the same bytes hold the histogram and then the band
+// entries of the request.
+template <int NQ, int NW, int CHUNK, bool FP8>
 struct IdxSmem {
   static constexpr int kTileBytes = FP8 ? 32 * 128 : 32 * 256;
-  static constexpr int kRing = (kIdxThreads / kWave) * 2 * kTileBytes;
-  static constexpr int kReuse = kSampleCap * 4 > kCandCap * 8 ? kSampleCap * 4 : kCandCap * 8;
+  static constexpr int kRing = NW * 2 * kTileBytes;
+  static constexpr int kReuse = kBandCap * 8 > kHistBins * 4 ? kBandCap * 8 : kHistBins * 4;
   static constexpr int kArena = kRing > kReuse ? kRing : kReuse;
   alignas(16) unsigned char arena[kArena];
   uint32_t keys[NQ * CHUNK];
   alignas(16) float w[NQ][64];
   float kscale[FP8 ? CHUNK : 1];
   int pages[CHUNK / 64];
-  uint32_t hist[256];
-  uint32_t cbase[kMaxChunksPerSeq + 1];
-  uint32_t sel[2];
+  uint32_t hist[256];                    // radix-select digits
+  uint32_t cbase[kMaxChunksPerSeq + 1];  // band entries before each chunk
+  uint32_t abase[kMaxChunksPerSeq + 1];  // keys >= hi before each chunk
+  uint32_t nabove[kMaxChunksPerSeq];     // keys >= hi per chunk
+  uint32_t bitmap[CHUNK / 32];           // selected positions of one chunk (whole-request writer)
+  uint32_t mm[NQ][NW][2];                // per-wave min / max valid key
+  uint32_t ref[NQ][2];                   // [lo, hi) of this chunk
+  uint32_t sel[4];
   uint32_t scan[16];
   uint32_t flag[4];
+  uint32_t next_tile;
 };
 
 template <bool FP8>
@@ -80,45 +95,110 @@ struct QOps<true> {
   int scale[2];
 };
 
-template <int NQ, int CHUNK, bool FP8>
-__global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeArgs a) {
-  __shared__ IdxSmem<NQ, CHUNK, FP8> sm;
-  uint32_t* s_keys = sm.keys;                                  // [NQ][CHUNK]
-  uint32_t* s_smp = reinterpret_cast<uint32_t*>(sm.arena);     // [kSampleCap] samples (after scoring)
+__device__ __forceinline__ void xstore64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t xload64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return (uint64_t)v | ((uint64_t)tag << 32); }
 
-  constexpr int NS = CHUNK / kSampleEvery;  // samples per chunk (CHUNK/kRun runs of kRun/kSampleEvery)
-  constexpr int NT = CHUNK / 32;            // 32-position tiles per chunk
-  constexpr int NW = kIdxThreads / kWave;
-  static_assert(NT % NW == 0, "tiles must split evenly over waves");
-  constexpr int RUNS = CHUNK / (NW * kRun);  // sorted runs per wave
-  static_assert(RUNS * NW * kRun == CHUNK, "the chunk splits into whole runs per wave");
+// Polls `n` tagged words until each carries `tag` (at most spin_max rounds
+// of sleeping).  Returns false on time-out.
+__device__ __forceinline__ bool poll_tagged(const uint64_t* p, int n, uint32_t tag, int spin_max, uint32_t* vals) {
+  int spins = 0;
+  for (;;) {
+    bool all = true;
+    for (int i = 0; i < n; ++i) {
+      const uint64_t v = xload64(&p[i]);
+      vals[i] = (uint32_t)v;
+      all &= (uint32_t)(v >> 32) == tag;
+    }
+    if (all) return true;
+    if (++spins > spin_max) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+template <int NQ, int NW, int CHUNK, bool FP8>
+__global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs a) {
+  __shared__ IdxSmem<NQ, NW, CHUNK, FP8> sm;
+  uint32_t* s_keys = sm.keys;  // [NQ][CHUNK]
+
+  constexpr int THREADS = NW * 64;
+  constexpr int NT = CHUNK / 32;  // 32-position tiles per chunk
+  static_assert(NT >= 2 * NW, "each wave starts with two tiles");
+  constexpr int PER = CHUNK / THREADS;  // keys per thread (contiguous positions)
+  static_assert(PER * THREADS == CHUNK && 32 % PER == 0, "chunk splits into whole bit groups per thread");
+  static_assert(kMaxChunksPerSeq <= THREADS, "one thread per chunk of a request");
 
   const int c = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 31, half = lane >> 5;
-
-  int L = a.seq_lens[b];
-  L = max(0, min(L, a.max_pages * 64));
-  const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
-  if (c >= n_chunks) return;
   const int t0 = b * NQ;
   const int s0 = c * CHUNK;
   const int* bt = a.block_table + (size_t)b * a.max_pages;
 
-  // ---------------------------------------------------------------- stage q, w, page ids
-  for (int i = tid; i < NQ * 64; i += kIdxThreads) sm.w[i / 64][i % 64] = a.w[(size_t)(t0 + i / 64) * 64 + i % 64];
-  for (int i = tid; i < CHUNK / 64; i += kIdxThreads) {
-    const int lp = s0 / 64 + i;
-    const int pg = lp < a.max_pages ? bt[lp] : 0;  // in bounds whatever L is: no wait on seq_lens first
-    sm.pages[i] = lp * 64 < L ? min(max(pg, 0), a.num_pages - 1) : 0;
-  }
-  if constexpr (FP8) {
-    __syncthreads();
-    for (int i = tid; i < CHUNK; i += kIdxThreads)
-      sm.kscale[i] = s0 + i < L ? a.k_scales[(size_t)sm.pages[i >> 6] * 64 + (i & 63)] : 0.f;
-  }
+  // ---------------------------------------------------------------- page ids (one memory latency)
+  // Page ids are loaded in bounds of the block table whatever the request's
+  // length, at the same time as the length itself.
+  int pg = 0;
+  if (tid < CHUNK / 64 && s0 / 64 + tid < a.max_pages) pg = bt[s0 / 64 + tid];
+  int L = a.seq_lens[b];
+  L = max(0, min(L, a.max_pages * 64));
+  const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
+  if (c >= n_chunks) return;
+  if (tid < CHUNK / 64) sm.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
+  const int n_valid = min(CHUNK, L - s0);     // positions of this chunk in the cache (>= 1)
+  const int nt_used = (n_valid + 31) / 32;    // tiles that hold any of them
+  if (tid == 0) sm.next_tile = 2 * NW;
+  __syncthreads();
 
+  // ---------------------------------------------------------------- score
+  // Tiles of 32 positions (inside one page) are dealt to the waves on demand
+  // (an LDS counter), so the chunk's waves finish together.  Each wave moves
+  // its tiles by direct-to-LDS loads into a private two-slot ring; each DMA
+  // instruction reads one contiguous kilobyte of the tile (eight lanes per
+  // 128-byte line) and writes lane l's 16 bytes to slot 64i + l; inside a
+  // line the 16-byte chunks are XOR-swizzled by (row & 7), so the MFMA
+  // operand reads (row n, fixed column) hit distinct banks.
+  constexpr int TB = IdxSmem<NQ, NW, CHUNK, FP8>::kTileBytes;
+  constexpr int DMA_PER_TILE = TB / 1024;
+  constexpr int ROW = FP8 ? 128 : 256;  // bytes per key row
+  constexpr int RPI = 1024 / ROW;       // rows per DMA instruction
+  unsigned char* ring = sm.arena + wid * 2 * TB;
+  // this lane's share of every DMA instruction: row (within the instruction)
+  // and the 16-byte chunk of that row
+  const int dma_row = lane / (64 / RPI);
+  const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
+  auto issue = [&](int tile, int slot_i) {
+    const int lp = tile * 32;  // position inside the chunk
+    const char* base =
+        static_cast<const char*>(a.k) + ((size_t)sm.pages[lp >> 6] * 64 + (lp & 32)) * ROW;
+    unsigned char* dst = ring + slot_i * TB;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_TILE; ++i) {
+      const int row = RPI * i + dma_row;
+      const int col = 8 * dma_line + ((lane & 7) ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
+    }
+  };
+  // the first two tiles of every wave are in flight while q, w and the FP8
+  // row scales load
+  int cur = wid, nxt = wid + NW;
+  if (cur < nt_used) issue(cur, 0);
+  if (nxt < nt_used) issue(nxt, 1);
+
+  for (int i = tid; i < NQ * 64; i += THREADS) sm.w[i / 64][i % 64] = a.w[(size_t)(t0 + i / 64) * 64 + i % 64];
+  if constexpr (FP8) {
+    for (int i = tid; i < CHUNK; i += THREADS)
+      sm.kscale[i] = i < n_valid ? a.k_scales[(size_t)sm.pages[i >> 6] * 64 + (i & 63)] : 0.f;
+  }
+  // tiles nobody scores hold no visible position: their keys are 0
+  for (int i = nt_used * 32 + tid; i < CHUNK; i += THREADS)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) s_keys[j * CHUNK + i] = 0u;
   QOps<FP8> qa[NQ * 2];  // A operands: the token's 64 heads as two 32-row tiles
 #pragma unroll
   for (int mt = 0; mt < NQ * 2; ++mt) {
@@ -144,54 +224,30 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
       }
     }
   }
-  __syncthreads();
+  // the request's epoch (advanced by the last workgroup of the previous
+  // call that exchanged for this request) tags this call's exchange words
+  uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
+  const uint32_t tag = xload(&ctr[kEpoch]) + 1u;
+  __syncthreads();  // w, FP8 row scales and zeroed keys visible
 
   int vis[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) vis[j] = max(0, L - NQ + j + 1);
-
-  // ---------------------------------------------------------------- score
-  // Wave w scores tiles w, w+NW, ... (32 positions each, inside one page).
-  // Tiles are moved by direct-to-LDS loads into a two-slot ring private to
-  // the wave.  Each DMA instruction reads one contiguous kilobyte of the tile
-  // (eight lanes per 128-byte line) and writes lane l's 16 bytes to slot
-  // 64i + l; inside a line the 16-byte chunks are XOR-swizzled by (row & 7),
-  // so the MFMA operand reads (row n, fixed column) hit distinct banks.
-  // Tiles past the end of the request copy a valid (clamped) tile and are
-  // masked afterwards.
-  constexpr int TB = IdxSmem<NQ, CHUNK, FP8>::kTileBytes;
-  constexpr int DMA_PER_TILE = TB / 1024;
-  constexpr int NIT = NT / NW;
-  constexpr int ROW = FP8 ? 128 : 256;             // bytes per key row
-  constexpr int RPI = 1024 / ROW;                  // rows per DMA instruction
-  unsigned char* ring = sm.arena + wid * 2 * TB;
-  auto tile_pos0 = [&](int it) { return s0 + (wid + NW * it) * 32; };
-  // this lane's share of every DMA instruction: row (within the instruction)
-  // and the 16-byte chunk of that row
-  const int dma_row = lane / (64 / RPI);
-  const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
-  auto issue = [&](int it) {
-    const int pos0 = tile_pos0(it);
-    const int lp = max(min(pos0, L - 1) - s0, 0);  // position inside the chunk, clamped
-    const char* base =
-        static_cast<const char*>(a.k) + ((size_t)sm.pages[lp >> 6] * 64 + (lp & 32)) * ROW;
-    unsigned char* dst = ring + (it & 1) * TB;
+  uint32_t kmin[NQ], kmax[NQ];  // this lane's smallest / largest valid key
 #pragma unroll
-    for (int i = 0; i < DMA_PER_TILE; ++i) {
-      const int row = RPI * i + dma_row;
-      const int col = 8 * dma_line + ((lane & 7) ^ (row & 7));
-      __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
-    }
-  };
+  for (int j = 0; j < NQ; ++j) {
+    kmin[j] = 0xffffffffu;
+    kmax[j] = 0u;
+  }
+
   // LDS byte offset of (row, 16-byte chunk) inside a tile
   auto slot = [&](int row, int col) {
     return 1024 * (row / RPI) + 16 * ((64 / RPI) * (row % RPI) + 8 * (col >> 3) + ((col & 7) ^ (row & 7)));
   };
 
-  auto compute = [&](int it) {
-    const int tile = wid + NW * it;
+  auto compute = [&](int tile, int slot_i) {
     const int pos0 = s0 + tile * 32;
-    const unsigned char* src = ring + (it & 1) * TB;
+    const unsigned char* src = ring + slot_i * TB;
     f32x16 acc[NQ * 2];
 #pragma unroll
     for (int mt = 0; mt < NQ * 2; ++mt) acc[mt] = (f32x16){};
@@ -217,7 +273,7 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
                                                                    qa[mt].scale[j], 0, 127);
       }
     }
-    const float kscale = FP8 ? sm.kscale[min(tile * 32 + n, CHUNK - 1)] : 1.f;
+    const float kscale = FP8 ? sm.kscale[tile * 32 + n] : 1.f;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       float part = 0.f;
@@ -235,313 +291,442 @@ __global__ __launch_bounds__(kIdxThreads) void li_decode_kernel(const IdxDecodeA
       if constexpr (FP8) part *= kscale;  // positive per-row scale commutes with ReLU
       if (half == 0) {
         const int s = pos0 + n;
-        s_keys[j * CHUNK + tile * 32 + n] = (s < vis[j]) ? score_key(part) : 0u;
+        const uint32_t key = (s < vis[j]) ? score_key(part) : 0u;
+        s_keys[j * CHUNK + tile * 32 + n] = key;
+        if (key != 0u) {
+          kmin[j] = min(kmin[j], key);
+          kmax[j] = max(kmax[j], key);
+        }
       }
     }
   };
 
-  issue(0);
-  if (NIT > 1) issue(1);
+  int slot_i = 0;
 #pragma unroll 1
-  for (int it = 0; it < NIT; ++it) {
-    // tile it has landed once at most the next tile's loads are outstanding
-    if (it + 1 < NIT) SLI_WAIT_VMCNT(DMA_PER_TILE);
+  while (cur < nt_used) {
+    // the current tile has landed once at most the next tile's loads are outstanding
+    if (nxt < nt_used) SLI_WAIT_VMCNT(DMA_PER_TILE);
     else SLI_WAIT_VMCNT(0);
-    compute(it);
-    if (it + 2 < NIT) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this slot's reads are done
-      issue(it + 2);
+    compute(cur, slot_i);
+    int g = nt_used;
+    if (nxt < nt_used) {
+      uint32_t t = 0;
+      if (lane == 0) t = atomicAdd(&sm.next_tile, 1u);
+      g = min(__builtin_amdgcn_readfirstlane(t), (uint32_t)nt_used);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this slot's operand reads are done
+      if (g < nt_used) issue(g, slot_i);
+    }
+    cur = nxt;
+    nxt = g;
+    slot_i ^= 1;
+  }
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const uint32_t mn = wave_min(kmin[j]), mx = wave_max(kmax[j]);
+    if (lane == 0) {
+      sm.mm[j][wid][0] = mn;
+      sm.mm[j][wid][1] = mx;
     }
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- samples
-  // Wave w sorts runs w, w+NW, ... (kRun consecutive keys each) in registers
-  // and publishes, per run, the keys at descending ranks 16i-1, i = 1..16:
-  // each certifies that the run holds >= 16i keys >= it.
+  // ---------------------------------------------------------------- selection
+  const int K = a.top_k;
   const size_t ncm = (size_t)a.n_chunks_max;
-#pragma unroll 1
-  for (int j = 0; j < NQ; ++j) {
-#pragma unroll 1
-    for (int r0 = 0; r0 < RUNS; ++r0) {
-      const int run = wid + NW * r0;
-      uint32_t v[kRun / kWave];
+  bool any_sel = false;
 #pragma unroll
-      for (int r = 0; r < kRun / kWave; ++r) v[r] = s_keys[j * CHUNK + kRun * run + (kRun / kWave) * lane + r];
-      wave_bitonic_sort_desc<kRun / kWave>(v);
-      // rank e = 4*lane + r; samples at e = 16i - 1, i.e. lanes 4i+3, register 3
-      uint32_t* smp = a.samples + ((size_t)(t0 + j) * ncm + c) * NS + (kRun / kSampleEvery) * run;
-      if ((lane & 3) == 3) xstore(&smp[lane >> 2], v[3]);
-    }
+  for (int j = 0; j < NQ; ++j) any_sel |= vis[j] > K;
+  // Tokens that see at most K positions keep them all: chunk c's positions go
+  // to out[s0 ...] (every earlier chunk is full); the chunk holding the last
+  // visible position pads the row with -1.
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    if (vis[j] > K) continue;
+    int32_t* out = a.idx_out + (size_t)(t0 + j) * K;
+    for (int i = tid; i < CHUNK; i += THREADS)
+      if (s0 + i < vis[j]) out[s0 + i] = s0 + i;
+    if (c == (vis[j] == 0 ? 0 : (vis[j] - 1) / CHUNK))
+      for (int i = vis[j] + tid; i < K; i += THREADS) out[i] = -1;
   }
-  wait_vmem();
-  __syncthreads();
-  // Publish: the block barrier orders every thread's sample stores before
-  // thread 0's agent-scope release; the wait polls with relaxed loads and
-  // acquires once.  One fence pair per workgroup, not per thread or per poll.
-  uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
-  if (tid == 0) {
-    fence_release_agent();
-    atomic_add_acq_rel(&ctr[0], 1u);
-    unsigned spins = 0, timed_out = 0;
-    while (atomic_load_relaxed(&ctr[0]) < (uint32_t)n_chunks) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinMax) {
-        timed_out = 1;
-        break;
-      }
-    }
-    fence_acquire_agent();
-    if (timed_out) atomic_add_acq_rel(&ctr[2], 1u);
-    sm.flag[0] = timed_out;
-  }
-  __syncthreads();
-  const bool timed_out = sm.flag[0] != 0;
+  if (!any_sel) return;  // (every workgroup of the request decides alike: no exchange)
 
-  // ---------------------------------------------------------------- lower bound and emission
-  const int m_need = (a.top_k + kSampleEvery - 1) / kSampleEvery;
-  constexpr int PER = CHUNK / kIdxThreads;
+  const int R = (K + n_chunks - 1) / n_chunks;
+
+  // 1. the interval [lo_c, hi_c) holding this chunk's R-th largest key
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sm.arena);  // [kHistBins] (the key ring is free now)
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
-    uint32_t tau = 1u;
-    const int n_samples = n_chunks * NS;
-    if (!timed_out && m_need <= n_samples) {
-      const uint32_t* smp = a.samples + (size_t)(t0 + j) * ncm * NS;
-      int ngt;
-      if (n_samples <= kSampleCap) {
-        // all loads in flight at once (a loop with one load per trip would
-        // pay the memory latency once per trip)
-        constexpr int PERS = kSampleCap / kIdxThreads;
-        uint32_t sv[PERS];
+    if (vis[j] <= K) continue;
+    const int valid = max(0, min(CHUNK, vis[j] - s0));
+    uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-        for (int r = 0; r < PERS; ++r) {
-          const int i = tid + r * kIdxThreads;
-          sv[r] = i < n_samples ? xload(&smp[i]) : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < PERS; ++r) {
-          const int i = tid + r * kIdxThreads;
-          if (i < n_samples) s_smp[i] = sv[r];
-        }
-        __syncthreads();
-        tau = block_radix_select<kSampleCap / kIdxThreads>([&](int i) { return s_smp[i]; }, n_samples, m_need, sm.hist,
-                                                           sm.sel, ngt);
-      } else {
-        tau = block_radix_select_big([&](int i) { return xload(&smp[i]); }, n_samples, m_need, sm.hist, sm.sel, ngt);
-      }
-      tau = max(tau, 1u);
+    for (int w = 0; w < NW; ++w) {
+      mn = min(mn, sm.mm[j][w][0]);
+      mx = max(mx, sm.mm[j][w][1]);
     }
+    if (valid < R) {
+      // fewer than R keys: lo_c = 1 makes the request's lo admit every valid
+      // key (more than K of them), and fewer than R keys are >= hi_c = 1
+      if (tid == 0) sm.ref[j][0] = 1u, sm.ref[j][1] = 1u;
+    } else if (mn == mx) {
+      if (tid == 0) sm.ref[j][0] = mn, sm.ref[j][1] = mn + 1u;
+    } else {
+      const int top = 31 - __clz(mn ^ mx);
+      const int shift = max(0, top - 11);
+      const uint32_t base = mn >> shift;  // bin of a key: (key >> shift) - base, < 4096
+      for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const uint32_t key = s_keys[j * CHUNK + tid * PER + i];
+        if (key != 0u) atomicAdd(&hist[(key >> shift) - base], 1u);
+      }
+      __syncthreads();
+      // thread t owns bins kHistBins-1 - BPT t - r, r < BPT (descending keys)
+      constexpr int BPT = kHistBins / THREADS;
+      uint32_t h[BPT], sum = 0;
+#pragma unroll
+      for (int r = 0; r < BPT; ++r) {
+        h[r] = hist[kHistBins - 1 - BPT * tid - r];
+        sum += h[r];
+      }
+      uint32_t tot;
+      const uint32_t before = block_excl_scan(sum, sm.scan, tot);
+      if (before < (uint32_t)R && (uint32_t)R <= before + sum) {
+        uint32_t acc = before;
+#pragma unroll
+        for (int r = 0; r < BPT; ++r) {
+          if (acc < (uint32_t)R && (uint32_t)R <= acc + h[r]) {
+            const uint32_t bin = (uint32_t)(kHistBins - 1 - BPT * tid - r) + base;
+            const uint64_t up = (uint64_t)(bin + 1u) << shift;
+            sm.ref[j][0] = bin << shift;
+            sm.ref[j][1] = up > 0xffffffffull ? 0xffffffffu : (uint32_t)up;
+          }
+          acc += h[r];
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t* rp = a.refs + ((size_t)(t0 + j) * ncm + c) * 2;
+      xstore64(&rp[0], tagged(sm.ref[j][0], tag));
+      xstore64(&rp[1], tagged(sm.ref[j][1], tag));
+    }
+  }
+
+  // exchange 1: every chunk's [lo_c, hi_c) -> the request's [lo, hi)
+  uint32_t lo_ref[NQ], hi_ref[NQ];
+  {
+    uint32_t l[NQ], h[NQ];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      l[j] = 0xffffffffu;
+      h[j] = 0u;
+      if (vis[j] > K && tid < n_chunks) {
+        uint32_t v[2];
+        ok &= poll_tagged(a.refs + ((size_t)(t0 + j) * ncm + tid) * 2, 2, tag, a.spin_max, v);
+        l[j] = v[0];
+        h[j] = v[1];
+      }
+    }
+    const bool refs_ok = __syncthreads_and(ok) != 0;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      l[j] = wave_min(l[j]);
+      h[j] = wave_max(h[j]);
+      if (lane == 0) {
+        sm.mm[j][wid][0] = l[j];
+        sm.mm[j][wid][1] = h[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      uint32_t lm = 0xffffffffu, hm = 0u;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        lm = min(lm, sm.mm[j][w][0]);
+        hm = max(hm, sm.mm[j][w][1]);
+      }
+      // a workgroup that did not see every chunk's interval in time treats
+      // all of its keys as band, which keeps the selection exact
+      lo_ref[j] = refs_ok ? max(lm, 1u) : 1u;
+      hi_ref[j] = refs_ok ? hm : 0xffffffffu;
+    }
+  }
+
+  // 2. publish keys >= hi (back of the region) and the band [lo, hi) (front),
+  //    both in position order, then the tagged counts
+#pragma unroll 1
+  for (int j = 0; j < NQ; ++j) {
+    if (vis[j] <= K) continue;
     uint32_t kk[PER];
-    uint32_t cnt = 0;
+    uint32_t na = 0, nb = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       kk[i] = s_keys[j * CHUNK + tid * PER + i];
-      cnt += kk[i] >= tau ? 1u : 0u;
+      na += kk[i] >= hi_ref[j] ? 1u : 0u;
+      nb += (kk[i] >= lo_ref[j] && kk[i] < hi_ref[j]) ? 1u : 0u;
     }
-    uint32_t total;
-    uint32_t off = block_excl_scan(cnt, sm.scan, total);
-    const size_t region = ((size_t)(t0 + j) * ncm + c) * CHUNK;
+    uint32_t tot;
+    const uint32_t off = block_excl_scan(na | (nb << 16), sm.scan, tot);  // both counts <= CHUNK < 2^16
+    uint32_t oa = off & 0xffffu, ob = off >> 16;
+    uint64_t* reg = a.cand + ((size_t)(t0 + j) * ncm + c) * CHUNK;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (kk[i] >= tau) {
-        xstore(&a.cand_key[region + off], kk[i]);
-        xstore(&a.cand_pos[region + off], s0 + tid * PER + i);
-        ++off;
+      const uint64_t e = (uint64_t)kk[i] | ((uint64_t)(uint32_t)(s0 + tid * PER + i) << 32);
+      if (kk[i] >= hi_ref[j]) {
+        xstore64(&reg[CHUNK - 1 - oa], e);
+        ++oa;
+      } else if (kk[i] >= lo_ref[j]) {
+        xstore64(&reg[ob], e);
+        ++ob;
       }
     }
-    if (tid == 0) xstore(&a.cand_cnt[(size_t)(t0 + j) * ncm + c], total);
-    __syncthreads();  // s_smp is reused by the next token's bound search
+    if (tid == 0) sm.flag[2 + (j & 1)] = tot;
   }
+  // the lists are complete in memory before the counts that announce them
   wait_vmem();
   __syncthreads();
+  uint32_t old2 = 0;
   if (tid == 0) {
-    fence_release_agent();
-    const bool last = atomic_add_acq_rel(&ctr[1], 1u) == (uint32_t)n_chunks - 1;
-    if (last) fence_acquire_agent();
-    sm.flag[1] = last ? 1u : 0u;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+      if (vis[j] > K) xstore64(&a.cnts[(size_t)(t0 + j) * ncm + c], tagged(sm.flag[2 + (j & 1)], tag));
+    old2 = __hip_atomic_fetch_add(&ctr[kArrive2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (!sm.flag[1]) return;
+  // exchange 2: every chunk's counts
+  uint32_t cnt_v[NQ];
+  {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      cnt_v[j] = 0u;
+      if (vis[j] > K && tid < n_chunks) ok &= poll_tagged(&a.cnts[(size_t)(t0 + j) * ncm + tid], 1, tag, a.spin_max, &cnt_v[j]);
+    }
+    const bool all_ok = __syncthreads_and(ok) != 0;
+    if (tid == 0) {
+      uint32_t mode = kModeNormal;
+      const bool last = old2 == (uint32_t)n_chunks - 1;
+      if (last) {
+        // last to arrive: writes the whole request if some workgroup gave up
+        const uint32_t st = __hip_atomic_fetch_or(&ctr[kState], kStLast, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (st & kStGaveUp) mode = kModeFull;
+      } else if (!all_ok) {
+        const uint32_t st = __hip_atomic_fetch_or(&ctr[kState], kStGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!(st & kStLast)) mode = kModeQuit;  // the last one has not arrived: it will write this share
+      }
+      sm.flag[1] = mode;
+      sm.flag[0] = all_ok ? 1u : 0u;
+      // done with the exchange state: the last to get here resets the line
+      // and advances the epoch (every workgroup read it at its start)
+      const uint32_t d = __hip_atomic_fetch_add(&ctr[kDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == (uint32_t)n_chunks - 1) {
+        __hip_atomic_store(&ctr[kArrive2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctr[kState], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctr[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctr[kEpoch], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t mode = sm.flag[1];
+  if (mode == kModeQuit) return;
+  if (sm.flag[0] == 0u) {
+    // the last one has arrived, so every count is in memory: read them again
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+      if (vis[j] > K && tid < n_chunks)
+        poll_tagged(&a.cnts[(size_t)(t0 + j) * ncm + tid], 1, tag, 1 << 30, &cnt_v[j]);
+    __syncthreads();
+  }
 
-  // ---------------------------------------------------------------- exact select (last workgroup)
-  uint32_t* s_ck = reinterpret_cast<uint32_t*>(sm.arena);  // [kCandCap] (the key ring is free now)
-  int* s_cp = reinterpret_cast<int*>(s_ck + kCandCap);       // [kCandCap]
-  const int K = a.top_k;
+  // 3. exact select among the band entries, then the writes
+  uint32_t* s_bk = reinterpret_cast<uint32_t*>(sm.arena);       // [kBandCap] band keys
+  int32_t* s_bp = reinterpret_cast<int32_t*>(s_bk + kBandCap);  // [kBandCap] their positions
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
+    if (vis[j] <= K) continue;
     const size_t tok = (size_t)(t0 + j);
-    uint32_t cc = tid < n_chunks ? xload(&a.cand_cnt[tok * ncm + tid]) : 0u;
-    uint32_t N;
-    uint32_t base = block_excl_scan(cc, sm.scan, N);
-    if (tid < n_chunks) sm.cbase[tid] = base;
-    if (tid == 0) sm.cbase[n_chunks] = N;
+    const uint32_t na_i = cnt_v[j] & 0xffffu, nb_i = cnt_v[j] >> 16;
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan(cnt_v[j], sm.scan, tot);
+    if (tid < n_chunks) {
+      sm.abase[tid] = pre & 0xffffu;
+      sm.cbase[tid] = pre >> 16;
+      sm.nabove[tid] = na_i;
+    }
+    if (tid == 0) {
+      sm.abase[n_chunks] = tot & 0xffffu;
+      sm.cbase[n_chunks] = tot >> 16;
+    }
+    (void)nb_i;
     __syncthreads();
-    // flat candidate f -> (chunk, slot) by binary search over the prefix offsets
-    // (only for the out-of-LDS fallback)
-    auto locate = [&](int f) {
+    const uint32_t A = tot & 0xffffu, NB = tot >> 16;
+    const int need = K - (int)A;  // >= 1: fewer than K keys reach hi
+    const bool in_lds = NB <= (uint32_t)kBandCap;
+    auto gaddr = [&](int i, uint32_t sl) { return (tok * ncm + i) * CHUNK + sl; };
+    // flat band entry f -> chunk (binary search over the prefix offsets)
+    auto chunk_of = [&](int f) {
       int lo = 0, hi = n_chunks;  // cbase[lo] <= f < cbase[hi]
       while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if ((int)sm.cbase[mid] <= f) lo = mid; else hi = mid;
       }
-      return (tok * ncm + lo) * CHUNK + (f - sm.cbase[lo]);
+      return lo;
     };
-    const bool in_lds = N <= (uint32_t)kCandCap;
     if (in_lds) {
-      // Chunk by chunk: thread i takes slot i (+256, ...) of each chunk's
-      // region, with the loads of 8 chunks in flight at once.
-      constexpr int GB = 8;
+      // up to eight loads per thread in flight at once (one memory latency
+      // per 8 x blockDim entries)
+      constexpr int LPT = kBandCap / THREADS < 8 ? kBandCap / THREADS : 8;
 #pragma unroll 1
-      for (int c0 = 0; c0 < n_chunks; c0 += GB) {
-        uint32_t maxc = 0;
-        for (int u = 0; u < GB && c0 + u < n_chunks; ++u) maxc = max(maxc, sm.cbase[c0 + u + 1] - sm.cbase[c0 + u]);
-#pragma unroll 1
-        for (uint32_t s0 = 0; s0 < maxc; s0 += kIdxThreads) {
-          uint32_t kv[GB];
-          int32_t pv[GB];
+      for (int f0 = 0; f0 < (int)NB; f0 += LPT * THREADS) {
+        uint64_t ev[LPT];
 #pragma unroll
-          for (int u = 0; u < GB; ++u) {
-            const int cc2 = c0 + u;
-            const uint32_t sl = s0 + tid;
-            const bool ok = cc2 < n_chunks && sl < sm.cbase[min(cc2 + 1, n_chunks)] - sm.cbase[min(cc2, n_chunks)];
-            const size_t ga = (tok * ncm + cc2) * CHUNK + sl;
-            kv[u] = ok ? xload(&a.cand_key[ga]) : 0u;
-            pv[u] = ok ? xload(&a.cand_pos[ga]) : -1;
+        for (int r = 0; r < LPT; ++r) {
+          const int f = f0 + tid + r * THREADS;
+          ev[r] = 0ull;
+          if (f < (int)NB) {
+            const int i = chunk_of(f);
+            ev[r] = xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
           }
+        }
 #pragma unroll
-          for (int u = 0; u < GB; ++u) {
-            const int cc2 = c0 + u;
-            const uint32_t sl = s0 + tid;
-            if (cc2 < n_chunks && sl < sm.cbase[cc2 + 1] - sm.cbase[cc2]) {
-              s_ck[sm.cbase[cc2] + sl] = kv[u];
-              s_cp[sm.cbase[cc2] + sl] = pv[u];
-            }
+        for (int r = 0; r < LPT; ++r) {
+          const int f = f0 + tid + r * THREADS;
+          if (f < (int)NB) {
+            s_bk[f] = (uint32_t)ev[r];
+            s_bp[f] = (int32_t)(ev[r] >> 32);
           }
         }
       }
       __syncthreads();
     }
-    auto key_at = [&](int f) { return in_lds ? s_ck[f] : xload(&a.cand_key[locate(f)]); };
-    auto pos_at = [&](int f) { return in_lds ? s_cp[f] : xload(&a.cand_pos[locate(f)]); };
-
-    uint32_t tau = 0u;
-    int ties = 0;
-    const bool take_all = N <= (uint32_t)K;
-    if (!take_all) {
-      int ngt;
-      tau = in_lds ? block_radix_select<kCandCap / kIdxThreads>(key_at, (int)N, K, sm.hist, sm.sel, ngt)
-                   : block_radix_select_big(key_at, (int)N, K, sm.hist, sm.sel, ngt);
-      ties = K - ngt;
-    }
+    auto key_at = [&](int f) -> uint32_t {
+      if (in_lds) return s_bk[f];
+      const int i = chunk_of(f);
+      return (uint32_t)xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
+    };
+    int ngt;
+    const uint32_t tau = in_lds ? block_radix_select<kBandCap / THREADS>(key_at, (int)NB, need, sm.hist, sm.sel, ngt)
+                                : block_radix_select_big(key_at, (int)NB, need, sm.hist, sm.sel, ngt);
+    const uint32_t ties = (uint32_t)(need - ngt);  // keys equal to tau that are taken, lowest positions first
     int32_t* out = a.idx_out + tok * K;
-    uint32_t written;
-    if (in_lds) {
-      // In position order, 256 candidates per round: wave ballots rank the
-      // ties at tau and then the selected candidates inside each wave, and
-      // per-wave counts (double-buffered by round parity) rank the waves.
-      const int wid_ = tid >> 6;
-      constexpr int NWV = kIdxThreads / kWave;
-      uint32_t base = 0, ties_before = 0;
-      for (int f0 = 0, rnd = 0; f0 < (int)N; f0 += kIdxThreads, ++rnd) {
-        const int f = f0 + tid;
-        const uint32_t key = f < (int)N ? s_ck[f] : 0u;
-        const bool gt = f < (int)N && (take_all || key > tau);
-        const bool tie = f < (int)N && !take_all && key == tau;
-        uint32_t* cnts = sm.scan + 8 * (rnd & 1);
-        const uint64_t mt = __ballot(tie);
-        if (lane == 0) cnts[wid_] = (uint32_t)__popcll(mt);
-        __syncthreads();
-        uint32_t tb = 0, tt = 0;
-        for (int w2 = 0; w2 < NWV; ++w2) {
-          const uint32_t x = cnts[w2];
-          tb += w2 < wid_ ? x : 0u;
-          tt += x;
-        }
-        const uint32_t tie_rank =
-            ties_before + tb + __builtin_amdgcn_mbcnt_hi((uint32_t)(mt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
-        const bool sel = gt || (tie && tie_rank < (uint32_t)ties);
-        const uint64_t m = __ballot(sel);
-        if (lane == 0) cnts[NWV + wid_] = (uint32_t)__popcll(m);
-        __syncthreads();
-        uint32_t before = 0, tot = 0;
-        for (int w2 = 0; w2 < NWV; ++w2) {
-          const uint32_t x = cnts[NWV + w2];
-          before += w2 < wid_ ? x : 0u;
-          tot += x;
-        }
-        if (sel) {
-          const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          out[base + before + r] = s_cp[f];
-        }
-        base += tot;
-        ties_before += tt;
+
+    if (mode == kModeNormal) {
+      // band entries before this chunk: how many are > tau, how many tie
+      uint32_t gt = 0, eq = 0;
+      for (int f = tid; f < (int)sm.cbase[c]; f += THREADS) {
+        const uint32_t key = key_at(f);
+        gt += key > tau ? 1u : 0u;
+        eq += key == tau ? 1u : 0u;
       }
-      written = base;
+      uint32_t gt_before, eq_before;
+      block_excl_scan(gt | (eq << 16), sm.scan, gt_before);  // both <= band size < 2^16
+      eq_before = gt_before >> 16;
+      gt_before &= 0xffffu;
+      const uint32_t off = sm.abase[c] + gt_before + min(ties, eq_before);
+      // own keys in position order
+      uint32_t kk[PER], nt = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        kk[i] = s_keys[j * CHUNK + tid * PER + i];
+        nt += (kk[i] == tau && kk[i] >= lo_ref[j] && kk[i] < hi_ref[j]) ? 1u : 0u;
+      }
+      uint32_t tt;
+      uint32_t tr = eq_before + block_excl_scan(nt, sm.scan, tt);
+      bool selv[PER];
+      uint32_t ns = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const bool band = kk[i] >= lo_ref[j] && kk[i] < hi_ref[j];
+        const bool tie = band && kk[i] == tau;
+        selv[i] = kk[i] >= hi_ref[j] || (band && (kk[i] > tau || (tie && tr < ties)));
+        tr += tie ? 1u : 0u;
+        ns += selv[i] ? 1u : 0u;
+      }
+      uint32_t nst;
+      uint32_t o = off + block_excl_scan(ns, sm.scan, nst);
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (selv[i]) out[o++] = s0 + tid * PER + i;
     } else {
-      // Each thread walks a contiguous segment of the (position-ordered)
-      // candidates: one scan ranks the ties at tau, one places the selected.
-      const int seg = ((int)N + kIdxThreads - 1) / kIdxThreads;
-      const int f_lo = min((int)N, tid * seg), f_hi = min((int)N, f_lo + seg);
-      uint32_t my_ties = 0;
-      if (!take_all)
-        for (int f = f_lo; f < f_hi; ++f) my_ties += key_at(f) == tau ? 1u : 0u;
-      uint32_t tie_tot;
-      uint32_t tie_rank = block_excl_scan(my_ties, sm.scan, tie_tot);
-      uint32_t my_sel = 0;
-      {
-        uint32_t tr = tie_rank;
-        for (int f = f_lo; f < f_hi; ++f) {
-          const uint32_t key = key_at(f);
-          const bool tie = !take_all && key == tau;
-          my_sel += (take_all || key > tau || (tie && tr < (uint32_t)ties)) ? 1u : 0u;
-          tr += tie ? 1u : 0u;
+      // kModeFull: the whole request, chunk by chunk, from the published
+      // lists (keys >= hi all taken; band entries by tau and tie rank)
+      uint32_t off = 0, eq_seen = 0;
+#pragma unroll 1
+      for (int i = 0; i < n_chunks; ++i) {
+        for (int wd = tid; wd < CHUNK / 32; wd += THREADS) sm.bitmap[wd] = 0u;
+        __syncthreads();
+        const int ci0 = i * CHUNK;
+        for (uint32_t e = tid; e < sm.nabove[i]; e += THREADS) {
+          const int pos = (int)(xload64(&a.cand[gaddr(i, CHUNK - 1 - e)]) >> 32);
+          atomicOr(&sm.bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
         }
-      }
-      uint32_t o = block_excl_scan(my_sel, sm.scan, written);
-      {
-        uint32_t tr = tie_rank;
-        for (int f = f_lo; f < f_hi; ++f) {
-          const uint32_t key = key_at(f);
-          const bool tie = !take_all && key == tau;
-          if (take_all || key > tau || (tie && tr < (uint32_t)ties)) out[o++] = pos_at(f);
-          tr += tie ? 1u : 0u;
+        const int f0 = (int)sm.cbase[i], f1 = (int)sm.cbase[i + 1];
+#pragma unroll 1
+        for (int fb = f0; fb < f1; fb += THREADS) {
+          const int f = fb + tid;
+          uint64_t ev = 0ull;
+          if (f < f1)
+            ev = in_lds ? ((uint64_t)s_bk[f] | ((uint64_t)(uint32_t)s_bp[f] << 32)) : xload64(&a.cand[gaddr(i, f - f0)]);
+          const uint32_t key = (uint32_t)ev;
+          const bool tie = f < f1 && key == tau;
+          uint32_t et;
+          const uint32_t rank = eq_seen + block_excl_scan(tie ? 1u : 0u, sm.scan, et);
+          if (f < f1 && (key > tau || (tie && rank < ties))) {
+            const int pos = (int)(ev >> 32);
+            atomicOr(&sm.bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
+          }
+          eq_seen += et;
         }
+        __syncthreads();
+        // emit in position order: thread t owns bits PER*t .. PER*t + PER-1
+        const uint32_t word = sm.bitmap[(PER * tid) >> 5];
+        const uint32_t bits = (word >> ((PER * tid) & 31)) & ((1u << PER) - 1u);
+        uint32_t et;
+        uint32_t o = off + block_excl_scan((uint32_t)__popc(bits), sm.scan, et);
+#pragma unroll
+        for (int r = 0; r < PER; ++r)
+          if ((bits >> r) & 1u) out[o++] = ci0 + PER * tid + r;
+        off += et;
+        __syncthreads();
       }
     }
-    for (int i = (int)written + tid; i < K; i += kIdxThreads) out[i] = -1;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // LDS band arrays and offsets are reused by the next token
   }
 }
 
-template <int NQ, int CHUNK, bool FP8>
+template <int NQ, int NW, int CHUNK, bool FP8>
 static hipError_t launch_one(const IdxDecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.n_chunks_max, a.B);
-  hipLaunchKernelGGL((li_decode_kernel<NQ, CHUNK, FP8>), grid, dim3(kIdxThreads), 0, stream, a);
+  hipLaunchKernelGGL((li_decode_kernel<NQ, NW, CHUNK, FP8>), grid, dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-// Positions per workgroup.  Larger chunks when the grid would not otherwise
-// fit on the chip at once (two workgroups per CU): with every workgroup of a
-// request resident, the cross-workgroup bound, the candidate exchange and the
-// final select run after the streaming instead of under its memory latency.
-int idx_decode_chunk(int B, int n_q, int max_pages, int cus) {
-  (void)n_q;
+// Positions per workgroup.  4096 (eight waves, one workgroup per CU) when
+// the grid still gives every CU a workgroup: each CU then streams the same
+// amount and the request's chunks finish together.  Smaller chunks (four
+// waves, two workgroups per CU) for small batches, and for bf16 two-token
+// calls, whose keys and key ring would not fit beside each other in LDS.
+int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus) {
   const long long maxlen = (long long)max_pages * 64;
-  const long long wgs1k = (long long)B * ((maxlen + 1023) / 1024);
-  return wgs1k > 2LL * cus ? 2048 : 1024;
+  auto wgs = [&](long long ch) { return (long long)B * ((maxlen + ch - 1) / ch); };
+  if ((n_q == 1 || fp8) && wgs(4096) >= cus) return 4096;
+  return wgs(1024) > 2LL * cus ? 2048 : 1024;
 }
 
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream) {
   if (chunk == 1024) {
-    if (a.n_q == 1) return fp8 ? launch_one<1, 1024, true>(a, stream) : launch_one<1, 1024, false>(a, stream);
-    if (a.n_q == 2) return fp8 ? launch_one<2, 1024, true>(a, stream) : launch_one<2, 1024, false>(a, stream);
+    if (a.n_q == 1) return fp8 ? launch_one<1, 4, 1024, true>(a, stream) : launch_one<1, 4, 1024, false>(a, stream);
+    if (a.n_q == 2) return fp8 ? launch_one<2, 4, 1024, true>(a, stream) : launch_one<2, 4, 1024, false>(a, stream);
   } else if (chunk == 2048) {
-    if (a.n_q == 1) return fp8 ? launch_one<1, 2048, true>(a, stream) : launch_one<1, 2048, false>(a, stream);
-    if (a.n_q == 2) return fp8 ? launch_one<2, 2048, true>(a, stream) : launch_one<2, 2048, false>(a, stream);
+    if (a.n_q == 1) return fp8 ? launch_one<1, 4, 2048, true>(a, stream) : launch_one<1, 4, 2048, false>(a, stream);
+    if (a.n_q == 2) return fp8 ? launch_one<2, 4, 2048, true>(a, stream) : launch_one<2, 4, 2048, false>(a, stream);
+  } else if (chunk == 4096) {
+    if (a.n_q == 1) return fp8 ? launch_one<1, 8, 4096, true>(a, stream) : launch_one<1, 8, 4096, false>(a, stream);
+    if (a.n_q == 2 && fp8) return launch_one<2, 8, 4096, true>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -11,7 +11,6 @@ constexpr int kCounterStride = 32;     // uint32 words per request (one 128-byte
 constexpr int kMaxSeqs = 4096;         // requests per call; sizes the fixed counter region
 constexpr int kMaxChunksPerSeq = 256;  // positions per request <= 256 chunks
 constexpr int kMaxSplitRows = 2048;    // index entries one attention workgroup may own
-constexpr int kSampleEvery = 16;       // indexer: one order-statistic sample per 16 ranks
 
 struct IdxDecodeArgs {
   int B, n_q, max_pages, num_pages, top_k, n_chunks_max;
@@ -23,12 +22,12 @@ struct IdxDecodeArgs {
   const void* k;
   const float* k_scales;
   int32_t* idx_out;
+  int spin_max;        // polls (each ~64 cycles of sleep) before an exchange wait gives up
   // workspace
-  uint32_t* counters;  // [B][kCounterStride]: arrivals after sampling, arrivals after emission, timeouts
-  uint32_t* samples;   // [T][n_chunks_max][chunk/kSampleEvery]
-  uint32_t* cand_key;  // [T][n_chunks_max][chunk]
-  int32_t* cand_pos;   // [T][n_chunks_max][chunk]
-  uint32_t* cand_cnt;  // [T][n_chunks_max]
+  uint32_t* counters;  // [B][kCounterStride]: arrivals, departures, give-up state, epoch
+  uint64_t* refs;      // [T][n_chunks_max][2]  per chunk lo, hi (each tagged with the call's epoch)
+  uint64_t* cnts;      // [T][n_chunks_max]     per chunk: keys >= hi | band keys << 16 (tagged)
+  uint64_t* cand;      // [T][n_chunks_max][chunk] (key | position << 32): band from the front, keys >= hi from the back
 };
 
 
@@ -58,7 +57,7 @@ struct SfaArgs {
   float* part_ml;  // [T][n_splits][H][2]   (running max in log2 units, sum)
 };
 
-int idx_decode_chunk(int B, int n_q, int max_pages, int cus);
+int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus);
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);

@@ -187,6 +187,55 @@ def test_repeated_calls_identical_many_chunks(li):
     _check_indices(case, fi, [0, 23], ores)
 
 
+@pytest.mark.parametrize("spin", [0, 3])
+@pytest.mark.parametrize("name", ["ragged3", "mtp2", "k2048", "fp8_g5_mtp2"])
+def test_exchange_fallbacks_stay_exact(li, monkeypatch, name, spin):
+    """The decode indexer's cross-workgroup exchanges with (almost) no patience:
+    most waits time out, so workgroups publish every key, give up their share
+    and leave the whole request to the last one to arrive.  Indices must still
+    equal the oracle's, and the exchange state must be left reset."""
+    monkeypatch.setenv("LI_SPIN_MAX", str(spin))
+    case = synth.Case(**SMALL[name])
+    g = GpuCase(case, attention=False)
+    ws = torch.zeros(li.li_score_topk_workspace_size(case.B, case.n_q, case.max_pages, case.top_k),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        idx = g.score_topk(li, workspace=ws)
+        torch.cuda.synchronize()
+        tokens = list(range(case.T))
+        _check_indices(case, idx.cpu().numpy(), tokens, oracle.run_tokens(case, tokens, with_attn=False))
+    # arrivals, departures and give-up state back at zero (word 4 is the epoch)
+    assert int(ws[: case.B * 128].view(torch.int32).view(case.B, 32)[:, :3].abs().sum()) == 0
+
+
+def test_positional_trend_band_beyond_lds(li):
+    """Scores that grow with position (the top K all sit in the last chunks):
+    the band between the chunks' bracketing keys then holds most positions,
+    more than the select keeps in LDS, and the exact select runs over the
+    published lists in global memory."""
+    L, K = 6000, 1000
+    case = synth.Case(seed=23, B=1, n_q=1, seq_lens=[L], top_k=K, H=16)
+    g = GpuCase(case, attention=False)
+    qv = np.ones((1, 64, 128), np.float32)
+    wv = np.full((1, 64), 0.5, np.float32)
+    m = (np.arange(L) * 128) // L  # ones in the first m(s) key entries
+    kv = (np.arange(128)[None, :] < m[:, None]).astype(np.float32)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).bfloat16().view(torch.int16)
+    g.q = bf(qv).cuda()
+    g.w = torch.from_numpy(wv).cuda()
+    pool = torch.zeros((case.num_pages, 64, 128), dtype=torch.int16)
+    bt = case.block_table()
+    for s0 in range(0, L, 64):
+        blk = kv[s0:s0 + 64]
+        pool[bt[0, s0 // 64], :blk.shape[0]] = bf(blk)
+    g.k_pool = pool.cuda()
+    idx = g.score_topk(li).cpu().numpy()
+    sc = oracle.index_scores(bf(qv[0]).numpy().view(np.uint16), wv[0], bf(kv).numpy().view(np.uint16), L)
+    ridx, n = oracle.topk(sc, K)
+    assert (idx[0] == np.sort(ridx[:n])).all()
+    assert idx[0].min() > L // 2  # the trend really puts the selection in the last chunks
+
+
 def test_prefill_all_equal_scores(li):
     case = synth.Case(seed=22, B=1, n_q=8, seq_lens=[5000], top_k=700, H=16)
     g = GpuCase(case, attention=False)
