@@ -62,13 +62,13 @@ enum : uint32_t { kModeNormal = 0u, kModeFull = 1u, kModeQuit = 2u };
 template <int NQ, int NW, int CHUNK, bool FP8>
 struct IdxSmem {
   static constexpr int kTileBytes = FP8 ? 32 * 128 : 32 * 256;
-  static constexpr int kRing = NW * 2 * kTileBytes;
+  static constexpr int kSlotBytes = kTileBytes + (FP8 ? 128 : 0);  // FP8: the tile's 32 row scales follow it
+  static constexpr int kRing = NW * 2 * kSlotBytes;
   static constexpr int kReuse = kBandCap * 8 > kHistBins * 4 ? kBandCap * 8 : kHistBins * 4;
   static constexpr int kArena = kRing > kReuse ? kRing : kReuse;
   alignas(16) unsigned char arena[kArena];
   uint32_t keys[NQ * CHUNK];
   alignas(16) float w[NQ][64];
-  float kscale[FP8 ? CHUNK : 1];
   int pages[CHUNK / 64];
   uint32_t hist[256];                    // radix-select digits
   uint32_t cbase[kMaxChunksPerSeq + 1];  // band entries before each chunk
@@ -140,65 +140,14 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   const int s0 = c * CHUNK;
   const int* bt = a.block_table + (size_t)b * a.max_pages;
 
-  // ---------------------------------------------------------------- page ids (one memory latency)
-  // Page ids are loaded in bounds of the block table whatever the request's
-  // length, at the same time as the length itself.
+  // ---------------------------------------------------------------- prologue (one memory latency)
+  // Page ids (loaded in bounds of the block table whatever the request's
+  // length), the length, q, w and the exchange epoch are all requested at
+  // once; the key tiles follow as soon as the page ids are in LDS.
   int pg = 0;
   if (tid < CHUNK / 64 && s0 / 64 + tid < a.max_pages) pg = bt[s0 / 64 + tid];
   int L = a.seq_lens[b];
-  L = max(0, min(L, a.max_pages * 64));
-  const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
-  if (c >= n_chunks) return;
-  if (tid < CHUNK / 64) sm.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
-  const int n_valid = min(CHUNK, L - s0);     // positions of this chunk in the cache (>= 1)
-  const int nt_used = (n_valid + 31) / 32;    // tiles that hold any of them
-  if (tid == 0) sm.next_tile = 2 * NW;
-  __syncthreads();
-
-  // ---------------------------------------------------------------- score
-  // Tiles of 32 positions (inside one page) are dealt to the waves on demand
-  // (an LDS counter), so the chunk's waves finish together.  Each wave moves
-  // its tiles by direct-to-LDS loads into a private two-slot ring; each DMA
-  // instruction reads one contiguous kilobyte of the tile (eight lanes per
-  // 128-byte line) and writes lane l's 16 bytes to slot 64i + l; inside a
-  // line the 16-byte chunks are XOR-swizzled by (row & 7), so the MFMA
-  // operand reads (row n, fixed column) hit distinct banks.
-  constexpr int TB = IdxSmem<NQ, NW, CHUNK, FP8>::kTileBytes;
-  constexpr int DMA_PER_TILE = TB / 1024;
-  constexpr int ROW = FP8 ? 128 : 256;  // bytes per key row
-  constexpr int RPI = 1024 / ROW;       // rows per DMA instruction
-  unsigned char* ring = sm.arena + wid * 2 * TB;
-  // this lane's share of every DMA instruction: row (within the instruction)
-  // and the 16-byte chunk of that row
-  const int dma_row = lane / (64 / RPI);
-  const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
-  auto issue = [&](int tile, int slot_i) {
-    const int lp = tile * 32;  // position inside the chunk
-    const char* base =
-        static_cast<const char*>(a.k) + ((size_t)sm.pages[lp >> 6] * 64 + (lp & 32)) * ROW;
-    unsigned char* dst = ring + slot_i * TB;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_TILE; ++i) {
-      const int row = RPI * i + dma_row;
-      const int col = 8 * dma_line + ((lane & 7) ^ (row & 7));
-      __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
-    }
-  };
-  // the first two tiles of every wave are in flight while q, w and the FP8
-  // row scales load
-  int cur = wid, nxt = wid + NW;
-  if (cur < nt_used) issue(cur, 0);
-  if (nxt < nt_used) issue(nxt, 1);
-
-  for (int i = tid; i < NQ * 64; i += THREADS) sm.w[i / 64][i % 64] = a.w[(size_t)(t0 + i / 64) * 64 + i % 64];
-  if constexpr (FP8) {
-    for (int i = tid; i < CHUNK; i += THREADS)
-      sm.kscale[i] = i < n_valid ? a.k_scales[(size_t)sm.pages[i >> 6] * 64 + (i & 63)] : 0.f;
-  }
-  // tiles nobody scores hold no visible position: their keys are 0
-  for (int i = nt_used * 32 + tid; i < CHUNK; i += THREADS)
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) s_keys[j * CHUNK + i] = 0u;
+  const float wv = tid < NQ * 64 ? a.w[(size_t)t0 * 64 + tid] : 0.f;
   QOps<FP8> qa[NQ * 2];  // A operands: the token's 64 heads as two 32-row tiles
 #pragma unroll
   for (int mt = 0; mt < NQ * 2; ++mt) {
@@ -228,7 +177,58 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   // call that exchanged for this request) tags this call's exchange words
   uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
   const uint32_t tag = xload(&ctr[kEpoch]) + 1u;
-  __syncthreads();  // w, FP8 row scales and zeroed keys visible
+  L = max(0, min(L, a.max_pages * 64));
+  const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
+  if (c >= n_chunks) return;
+  if (tid < CHUNK / 64) sm.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
+  if (tid < NQ * 64) sm.w[tid / 64][tid % 64] = wv;
+  const int n_valid = min(CHUNK, L - s0);     // positions of this chunk in the cache (>= 1)
+  const int nt_used = (n_valid + 31) / 32;    // tiles that hold any of them
+  if (tid == 0) sm.next_tile = 2 * NW;
+  // tiles nobody scores hold no visible position: their keys are 0
+  for (int i = nt_used * 32 + tid; i < CHUNK; i += THREADS)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) s_keys[j * CHUNK + i] = 0u;
+  __syncthreads();
+
+  // ---------------------------------------------------------------- score
+  // Tiles of 32 positions (inside one page) are dealt to the waves on demand
+  // (an LDS counter), so the chunk's waves finish together.  Each wave moves
+  // its tiles by direct-to-LDS loads into a private two-slot ring; each DMA
+  // instruction reads one contiguous kilobyte of the tile (eight lanes per
+  // 128-byte line) and writes lane l's 16 bytes to slot 64i + l; inside a
+  // line the 16-byte chunks are XOR-swizzled by (row & 7), so the MFMA
+  // operand reads (row n, fixed column) hit distinct banks.  FP8 tiles bring
+  // their 32 row scales along (one more direct-to-LDS load, 4 bytes a lane).
+  constexpr int TB = IdxSmem<NQ, NW, CHUNK, FP8>::kTileBytes;
+  constexpr int SB = IdxSmem<NQ, NW, CHUNK, FP8>::kSlotBytes;
+  constexpr int DMA_PER_TILE = TB / 1024 + (FP8 ? 1 : 0);
+  constexpr int ROW = FP8 ? 128 : 256;  // bytes per key row
+  constexpr int RPI = 1024 / ROW;       // rows per DMA instruction
+  unsigned char* ring = sm.arena + wid * 2 * SB;
+  // this lane's share of every DMA instruction: row (within the instruction)
+  // and the 16-byte chunk of that row
+  const int dma_row = lane / (64 / RPI);
+  const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
+  auto issue = [&](int tile, int slot_i) {
+    const int lp = tile * 32;  // position inside the chunk
+    const size_t row0 = (size_t)sm.pages[lp >> 6] * 64 + (lp & 32);
+    const char* base = static_cast<const char*>(a.k) + row0 * ROW;
+    unsigned char* dst = ring + slot_i * SB;
+#pragma unroll
+    for (int i = 0; i < TB / 1024; ++i) {
+      const int row = RPI * i + dma_row;
+      const int col = 8 * dma_line + ((lane & 7) ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
+    }
+    if constexpr (FP8) {
+      if (lane < 32) __builtin_amdgcn_global_load_lds(a.k_scales + row0 + lane, (lds_void*)(dst + TB), 4, 0, 0);
+    }
+  };
+  // the first two tiles of every wave
+  int cur = wid, nxt = wid + NW;
+  if (cur < nt_used) issue(cur, 0);
+  if (nxt < nt_used) issue(nxt, 1);
 
   int vis[NQ];
 #pragma unroll
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
 
   auto compute = [&](int tile, int slot_i) {
     const int pos0 = s0 + tile * 32;
-    const unsigned char* src = ring + slot_i * TB;
+    const unsigned char* src = ring + slot_i * SB;
     f32x16 acc[NQ * 2];
 #pragma unroll
     for (int mt = 0; mt < NQ * 2; ++mt) acc[mt] = (f32x16){};
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
                                                                    qa[mt].scale[j], 0, 127);
       }
     }
-    const float kscale = FP8 ? sm.kscale[tile * 32 + n] : 1.f;
+    const float kscale = FP8 ? reinterpret_cast<const float*>(src + TB)[n] : 1.f;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       float part = 0.f;
