@@ -3,7 +3,6 @@ for gfx950.  Usage: python -m sparse_attention_li_amd.build"""
 from __future__ import annotations
 
 import os
-import re
 import subprocess
 import sys
 
@@ -23,23 +22,23 @@ HIP_FLAGS = [
 
 
 # Kernels whose LDS operand reads are issued as instructions of their own and
-# awaited by explicit lgkmcnt waits: the compiler does not know such a register
-# is still being written until the wait, so a spill or copy of it in between
-# would read it early.  They must compile without any scratch.
-NO_SCRATCH = {"sfa.hip": ("sfa_bf16_kernel",)}
+# awaited by explicit lgkmcnt waits: the compiler does not know such a
+# register is still being written until the wait, so the build scans their
+# assembly for any use of it in between (lds_hazards.py).
+LDS_CHECKED = {"sfa.hip": ("sfa_bf16_kernel",)}
 
 
-def check_no_scratch(src: str, remarks: list, kernels: tuple) -> None:
-    name = None
-    for line in remarks:
-        m = re.search(r"Function Name: (\S+)", line)
-        if m:
-            name = m.group(1)
-            continue
-        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
-        if m and name and any(k in name for k in kernels) and int(m.group(1)) != 0:
-            raise RuntimeError(f"{src}: {name} uses {m.group(1)} bytes of scratch per lane; "
-                               "its explicitly awaited LDS reads require a spill-free build")
+def check_lds_hazards(src: str, inc: list, kernels: tuple) -> None:
+    from sparse_attention_li_amd import lds_hazards
+    out = os.path.join(HERE, "_build", os.path.splitext(src)[0] + ".gfx950.s")
+    cmd = ["hipcc", *HIP_FLAGS, *inc, "-S", "--cuda-device-only", "-x", "hip", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    found = lds_hazards.check_asm(open(out).read(), kernels)
+    if found:
+        lines = "\n".join(f"  {k}: {t}   ({reg})" for k, t, reg in found[:20])
+        raise RuntimeError(f"{src}: registers of in-flight LDS reads are used before their wait:\n{lines}")
 
 
 def build(verbose: bool = False) -> str:
@@ -50,17 +49,15 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        usage = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SCRATCH else []
-        cmd = ["hipcc", *HIP_FLAGS, *usage, *inc, "-c", *lang, os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *HIP_FLAGS, *inc, "-c", *lang, os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
-        lines = (r.stderr or "").splitlines()
-        msgs = [l for l in lines if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l]
+        msgs = [l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l]
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
-        if src in NO_SCRATCH:
-            check_no_scratch(src, lines, NO_SCRATCH[src])
+        if src in LDS_CHECKED:
+            check_lds_hazards(src, inc, LDS_CHECKED[src])
         if msgs and verbose:
             print("\n".join(msgs))
         objs.append(obj)
