@@ -61,7 +61,7 @@ IdxLayout idx_layout(int B, int n_q, bool fp8, int max_pages) {
   // geometry, so a workspace reused for another batch shape never finds the
   // previous call's lists where it expects zeroed counters.
   l.off_counters = o;
-  o = round_up(o + (size_t)sli::kMaxSeqs * sli::kCounterStride * 4, 256);
+  o = round_up(o + (size_t)(sli::kMaxSeqs + 1) * sli::kCounterStride * 4, 256);  // + the launch line
   l.off_refs = o;
   o = round_up(o + T * l.ncm * 2 * 8, 256);
   l.off_cnts = o;

@@ -47,12 +47,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kHistBins = 4096;  // LDS histogram that brackets a chunk's R-th largest key
 constexpr int kBandCap = 4096;   // band entries the final select keeps in LDS
 
-// Per-request words of the fixed counter region (one 128-byte line each).
-// Exchange data carries a per-call tag (the request's epoch + 1) in its upper
-// 32 bits, so a reader polls the data itself: no counter, no fence on the
-// common path.  The counters only settle the rare give-up fallback and let
-// the last workgroup to leave reset the line and advance the epoch.
-enum : uint32_t { kArrive2 = 0, kDone = 1, kState = 2, kEpoch = 4 };
+// Words of the fixed counter region (one 128-byte line per request, then one
+// line for the whole launch).  Exchange data carries a per-call tag (the
+// launch epoch + 1) in its upper 32 bits, so a reader polls the data itself:
+// no counter, no fence on the common path.  The epoch is one for the whole
+// workspace, so no word left by an earlier call -- for any request and any
+// batch shape -- carries the current tag.  The per-request counters only
+// settle the rare give-up fallback; the launch line counts departing
+// workgroups, and the last one advances the epoch.
+enum : uint32_t { kArrive2 = 0, kDone = 1, kState = 2 };
+enum : uint32_t { kGridDone = 0, kGridEpoch = 1 };
 enum : uint32_t { kStLast = 1u, kStGaveUp = 2u };
 enum : uint32_t { kModeNormal = 0u, kModeFull = 1u, kModeQuit = 2u };
 
@@ -66,10 +70,7 @@ struct IdxSmem {
   static constexpr int kRing = NW * 2 * kSlotBytes;
   static constexpr int kReuse = kBandCap * 8 > kHistBins * 4 ? kBandCap * 8 : kHistBins * 4;
   static constexpr int kArena = kRing > kReuse ? kRing : kReuse;
-  alignas(16) unsigned char arena[kArena];
-  uint32_t keys[NQ * CHUNK];
   alignas(16) float w[NQ][64];
-  int pages[CHUNK / 64];
   uint32_t hist[256];                    // radix-select digits
   uint32_t cbase[kMaxChunksPerSeq + 1];  // band entries before each chunk
   uint32_t abase[kMaxChunksPerSeq + 1];  // keys >= hi before each chunk
@@ -81,6 +82,17 @@ struct IdxSmem {
   uint32_t scan[16];
   uint32_t flag[4];
   uint32_t next_tile;
+};
+
+// The LDS object the key DMA writes (the ring) and the ones the streaming
+// loop reads or writes besides it (page ids, keys) are separate variables: the compiler's wait insertion then sees that those reads cannot
+// alias a tile still in flight and does not drain the loads before them.
+template <int NQ, int NW, int CHUNK, bool FP8>
+struct IdxLds {
+  IdxSmem<NQ, NW, CHUNK, FP8>& sm;
+  unsigned char* arena;  // [kArena]: key ring; after scoring the histogram, then the band entries
+  uint32_t* keys;        // [NQ][CHUNK]
+  int* pages;            // [CHUNK / 64]
 };
 
 template <bool FP8>
@@ -115,9 +127,10 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t* p, int n, uint32_t t
 }
 
 template <int NQ, int NW, int CHUNK, bool FP8>
-__global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs a) {
-  __shared__ IdxSmem<NQ, NW, CHUNK, FP8> sm;
-  uint32_t* s_keys = sm.keys;  // [NQ][CHUNK]
+__device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ, NW, CHUNK, FP8> lds,
+                                               const uint32_t tag) {
+  IdxSmem<NQ, NW, CHUNK, FP8>& sm = lds.sm;
+  uint32_t* s_keys = lds.keys;  // [NQ][CHUNK]
 
   constexpr int THREADS = NW * 64;
   constexpr int NT = CHUNK / 32;  // 32-position tiles per chunk
@@ -167,14 +180,11 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
       }
     }
   }
-  // the request's epoch (advanced by the last workgroup of the previous
-  // call that exchanged for this request) tags this call's exchange words
   uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
-  const uint32_t tag = xload(&ctr[kEpoch]) + 1u;
   L = max(0, min(L, a.max_pages * 64));
   const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
   if (c >= n_chunks) return;
-  if (tid < CHUNK / 64) sm.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
+  if (tid < CHUNK / 64) lds.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
   if (tid < NQ * 64) sm.w[tid / 64][tid % 64] = wv;
   const int n_valid = min(CHUNK, L - s0);     // positions of this chunk in the cache (>= 1)
   const int nt_used = (n_valid + 31) / 32;    // tiles that hold any of them
@@ -199,14 +209,14 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   constexpr int DMA_PER_TILE = TB / 1024 + (FP8 ? 1 : 0);
   constexpr int ROW = FP8 ? 128 : 256;  // bytes per key row
   constexpr int RPI = 1024 / ROW;       // rows per DMA instruction
-  unsigned char* ring = sm.arena + wid * 2 * SB;
+  unsigned char* ring = lds.arena + wid * 2 * SB;
   // this lane's share of every DMA instruction: row (within the instruction)
   // and the 16-byte chunk of that row
   const int dma_row = lane / (64 / RPI);
   const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
   auto issue = [&](int tile, int slot_i) {
     const int lp = tile * 32;  // position inside the chunk
-    const size_t row0 = (size_t)sm.pages[lp >> 6] * 64 + (lp & 32);
+    const size_t row0 = (size_t)lds.pages[lp >> 6] * 64 + (lp & 32);
     const char* base = static_cast<const char*>(a.k) + row0 * ROW;
     unsigned char* dst = ring + slot_i * SB;
 #pragma unroll
@@ -219,10 +229,28 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
       if (lane < 32) __builtin_amdgcn_global_load_lds(a.k_scales + row0 + lane, (lds_void*)(dst + TB), 4, 0, 0);
     }
   };
-  // the first two tiles of every wave
-  int cur = wid, nxt = wid + NW;
-  if (cur < nt_used) issue(cur, 0);
-  if (nxt < nt_used) issue(nxt, 1);
+  // `issued` counts this wave's vector-memory instructions; mark[s] is the
+  // count just after slot s's tile was issued.
+  uint32_t issued = 0, mark[2] = {0u, 0u};
+  auto issue_counted = [&](int tile, int slot_i) {
+    issue(tile, slot_i);
+    issued += DMA_PER_TILE;
+    mark[slot_i] = issued;
+  };
+  // The tile counter is bumped by an LDS atomic written as the instruction
+  // itself (with its own wait): as a compiler atomic it would make the wait
+  // pass drain every direct-to-LDS load in flight first.
+  const uint32_t next_addr = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)&sm.next_tile;
+  auto grab = [&]() -> int {
+    uint32_t t = 0;
+    if (lane == 0)  // one lane: one tile
+      asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(t) : "v"(next_addr), "v"(1u) : "memory");
+    return (int)min(__builtin_amdgcn_readfirstlane(t), (uint32_t)nt_used);
+  };
+  // the first two tiles of every wave; the one after them is dealt now
+  int cur = wid, nxt = wid + NW, pre = nt_used;
+  if (cur < nt_used) issue_counted(cur, 0);
+  if (nxt < nt_used) issue_counted(nxt, 1);
 
   int vis[NQ];
 #pragma unroll
@@ -295,23 +323,31 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
     }
   };
 
+  if (nxt < nt_used) pre = grab();
   int slot_i = 0;
 #pragma unroll 1
   while (cur < nt_used) {
-    // the current tile has landed once at most the next tile's loads are outstanding
-    if (nxt < nt_used) SLI_WAIT_VMCNT(DMA_PER_TILE);
-    else SLI_WAIT_VMCNT(0);
+    // the current tile has landed once at most the instructions issued after
+    // its DMA are outstanding (wave-uniform count: 0 or one tile's DMA)
+    switch (min(issued - mark[slot_i], 2u * DMA_PER_TILE + 2u)) {
+#define SLI_WAIT_CASE(N) case N: SLI_WAIT_VMCNT(N); break;
+      SLI_WAIT_CASE(0) SLI_WAIT_CASE(1) SLI_WAIT_CASE(2) SLI_WAIT_CASE(3) SLI_WAIT_CASE(4) SLI_WAIT_CASE(5)
+      SLI_WAIT_CASE(6) SLI_WAIT_CASE(7) SLI_WAIT_CASE(8) SLI_WAIT_CASE(9) SLI_WAIT_CASE(10) SLI_WAIT_CASE(11)
+      SLI_WAIT_CASE(12) SLI_WAIT_CASE(13) SLI_WAIT_CASE(14) SLI_WAIT_CASE(15) SLI_WAIT_CASE(16) SLI_WAIT_CASE(17)
+      SLI_WAIT_CASE(18)
+#undef SLI_WAIT_CASE
+      default: SLI_WAIT_VMCNT(0); break;
+    }
     compute(cur, slot_i);
     int g = nt_used;
-    if (nxt < nt_used) {
-      uint32_t t = 0;
-      if (lane == 0) t = atomicAdd(&sm.next_tile, 1u);
-      g = min(__builtin_amdgcn_readfirstlane(t), (uint32_t)nt_used);
+    if (pre < nt_used) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this slot's operand reads are done
-      if (g < nt_used) issue(g, slot_i);
+      issue_counted(pre, slot_i);
+      g = grab();
     }
     cur = nxt;
-    nxt = g;
+    nxt = pre;
+    pre = g;
     slot_i ^= 1;
   }
 #pragma unroll
@@ -347,7 +383,7 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   const int R = (K + n_chunks - 1) / n_chunks;
 
   // 1. the interval [lo_c, hi_c) holding this chunk's R-th largest key
-  uint32_t* hist = reinterpret_cast<uint32_t*>(sm.arena);  // [kHistBins] (the key ring is free now)
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lds.arena);  // [kHistBins] (the key ring is free now)
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
     if (vis[j] <= K) continue;
@@ -513,14 +549,12 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
       }
       sm.flag[1] = mode;
       sm.flag[0] = all_ok ? 1u : 0u;
-      // done with the exchange state: the last to get here resets the line
-      // and advances the epoch (every workgroup read it at its start)
+      // done with the request's exchange state: the last to get here resets it
       const uint32_t d = __hip_atomic_fetch_add(&ctr[kDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == (uint32_t)n_chunks - 1) {
         __hip_atomic_store(&ctr[kArrive2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctr[kState], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctr[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctr[kEpoch], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
@@ -537,7 +571,7 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   }
 
   // 3. exact select among the band entries, then the writes
-  uint32_t* s_bk = reinterpret_cast<uint32_t*>(sm.arena);       // [kBandCap] band keys
+  uint32_t* s_bk = reinterpret_cast<uint32_t*>(lds.arena);       // [kBandCap] band keys
   int32_t* s_bp = reinterpret_cast<int32_t*>(s_bk + kBandCap);  // [kBandCap] their positions
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
@@ -689,6 +723,27 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
       }
     }
     __syncthreads();  // LDS band arrays and offsets are reused by the next token
+  }
+}
+
+template <int NQ, int NW, int CHUNK, bool FP8>
+__global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs a) {
+  __shared__ IdxSmem<NQ, NW, CHUNK, FP8> sm;
+  __shared__ __attribute__((aligned(16))) unsigned char arena[IdxSmem<NQ, NW, CHUNK, FP8>::kArena];
+  __shared__ uint32_t keys[NQ * CHUNK];
+  __shared__ int pages[CHUNK / 64];
+  uint32_t* grid_line = a.counters + (size_t)kMaxSeqs * kCounterStride;
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(xload(&grid_line[kGridEpoch]) + 1u);
+  li_decode_body<NQ, NW, CHUNK, FP8>(a, IdxLds<NQ, NW, CHUNK, FP8>{sm, arena, keys, pages}, tag);
+  // every workgroup (those without work included) departs once; the last
+  // resets the count and advances the epoch for the next call
+  if (threadIdx.x == 0) {
+    const uint32_t total = gridDim.x * gridDim.y;
+    const uint32_t d = __hip_atomic_fetch_add(&grid_line[kGridDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == total - 1) {
+      __hip_atomic_store(&grid_line[kGridDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&grid_line[kGridEpoch], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
