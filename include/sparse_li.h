@@ -104,14 +104,16 @@ li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* strea
  *             score, ties going to the lower position, written in ascending
  *             position order; the rest of the row is -1.
  *   workspace li_score_topk_workspace_size(...) bytes, zero before its first use
- *             (see li_workspace_zero).  Its first 512 KiB hold per-request
- *             arrival counters at a fixed place for any geometry; each call
- *             leaves them zero, so one workspace can serve calls of different
+ *             (see li_workspace_zero).  Its first 512 KiB + 128 bytes hold
+ *             per-request exchange counters and one launch-wide epoch at a fixed
+ *             place for any geometry; each call leaves the counters zero and
+ *             advances the epoch, so one workspace can serve calls of different
  *             shapes.  Calls that share a workspace must not overlap in time.
  *             num_seqs <= 4096.
  *
- * Scores live only on chip: per-chunk candidate (key, position) lists above a
- * provable lower bound on the K-th score are the only intermediate in HBM.
+ * Scores live only on chip: the intermediates in HBM are, per chunk of
+ * positions, two bounds on the K-th score, the positions above the upper bound
+ * and the (key, position) band between the bounds.
  * Supported: q_per_seq in {1, 2} (decode, two-token verification; bf16 or
  * FP8) and q_per_seq >= 3 (prefill chunk; bf16, the workspace is not used
  * and may be NULL).
