@@ -51,6 +51,12 @@ def lib():
         L.oracle_topk.restype = i64
         L.oracle_sparse_attn.argtypes = [vp, i64, i32, vp, vp, i32, vp, i64, dbl, vp, vp, vp]
         L.oracle_sparse_attn.restype = None
+        L.oracle_encode_e4m3.argtypes = [dbl]
+        L.oracle_encode_e4m3.restype = ctypes.c_uint8
+        L.oracle_quant_mxfp8.argtypes = [vp, i64, i64, vp, vp]
+        L.oracle_quant_mxfp8.restype = None
+        L.oracle_quant_fp8_rows.argtypes = [vp, i64, i64, i64, vp, vp]
+        L.oracle_quant_fp8_rows.restype = None
         _LIB = L
     return _LIB
 
@@ -73,6 +79,32 @@ def e4m3(code: int) -> float:
 
 def e8m0(code: int) -> float:
     return lib().oracle_e8m0(int(code))
+
+
+def encode_e4m3(v: float) -> int:
+    """Nearest E4M3FN code (ties to the even code), saturating at 448."""
+    return int(lib().oracle_encode_e4m3(float(v)))
+
+
+def quant_mxfp8(x):
+    """x [n, L] bf16 bits (L % 32 == 0) -> (E4M3 codes [n, L], E8M0 scales [n, L/32])."""
+    x = _c(x, np.uint16)
+    n, L = x.shape
+    codes = np.empty((n, L), dtype=np.uint8)
+    scales = np.empty((n, L // 32), dtype=np.uint8)
+    lib().oracle_quant_mxfp8(_p(x), n, L, _p(codes), _p(scales))
+    return codes, scales
+
+
+def quant_fp8_rows(x, block: int):
+    """x [n, L] bf16 bits -> (E4M3 codes [n, L], f32 scales [n, ceil(L/block)])."""
+    x = _c(x, np.uint16)
+    n, L = x.shape
+    nb = (L + block - 1) // block
+    codes = np.empty((n, L), dtype=np.uint8)
+    scales = np.empty((n, nb), dtype=np.float32)
+    lib().oracle_quant_fp8_rows(_p(x), n, L, block, _p(codes), _p(scales))
+    return codes, scales
 
 
 def index_scores(q, w, k, vis: int, q_fmt="bf16", q_scales=None, k_fmt="bf16", k_scales=None) -> np.ndarray:

@@ -175,3 +175,101 @@ void oracle_sparse_attn(const uint16_t* q, int64_t H, int c_fmt, const void* c, 
     free(l);
   }
 }
+
+/*
+ * Quantisers and the cache append (the step before the path in every decode
+ * step: "Day-0 Inference Adaptation and Optimization for Hybrid Attention
+ * Architectures", sec. 4 -- MXFP8 indexer query with group 32, FP8 KV cache
+ * with per-token-head-tile scales of tile 128; "Optimizing Inference for
+ * Hybrid Attention LLMs", sec. 4 table; "Day0 Inference Adaptation and
+ * Performance Optimization for a Sparse Hybrid Architecture LLM", sec. 3.1 --
+ * quantised indexer q and K; the new token's cache rows are written into the
+ * paged cache).  Readings where the pages are silent:
+ *  - E4M3 encoding is round-to-nearest, ties to the even code, saturating
+ *    at +-448 (OCP E4M3FN has no infinity; "satfinite");
+ *  - MXFP8 (OCP Microscaling v1.0): per group of 32, shared exponent
+ *    X = 2^(floor(log2 amax) - 8) (8 = the largest E4M3 exponent), stored as
+ *    E8M0 code floor(log2 amax) - 8 + 127; an all-zero group takes X = 1;
+ *    elements are x / X encoded as E4M3;
+ *  - FP8 cache rows: f32 scale = amax / 448 of the row (or of each 128-wide
+ *    tile, the fifth tile of a 576-wide latent row being 64 wide), 1 for an
+ *    all-zero block; elements are fl32(x / scale) encoded as E4M3.  The
+ *    quotient is taken in fp32 (the kernel's precision decides the code).
+ */
+
+/* Nearest E4M3FN code of v (ties to the even code), saturating at 448. */
+uint8_t oracle_encode_e4m3(double v) {
+  const uint8_t sign = (v < 0 || (v == 0 && signbit(v))) ? 0x80 : 0;
+  double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7e;
+  /* magnitude in units of the code grid: below 2^-6 the grid step is 2^-9
+   * (subnormals and the smallest binade), above it 2^(e-3) for a in [2^e, 2^(e+1)) */
+  int e;
+  (void)frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  int ee = e - 1;      /* a in [2^ee, 2^(ee+1)) */
+  if (a == 0.0 || ee < -6) ee = -6;
+  const double step = ldexp(1.0, ee - 3);
+  double units = a / step;           /* exact: a power-of-two division */
+  double fl = floor(units);
+  double frac = units - fl;
+  double r = fl;
+  if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) r = fl + 1.0;
+  /* r * step is the rounded magnitude; re-derive the code from it */
+  double m = r * step;
+  if (m >= 448.0) return sign | 0x7e;
+  if (m == 0.0) return sign;
+  int e2;
+  (void)frexp(m, &e2);
+  int ex = e2 - 1; /* m in [2^ex, 2^(ex+1)) */
+  if (ex < -6) {   /* subnormal: m = k * 2^-9, k in 1..7 */
+    return sign | (uint8_t)(int)ldexp(m, 9);
+  }
+  int mant = (int)(ldexp(m, -ex) * 8.0) - 8; /* 0..7 */
+  return sign | (uint8_t)(((ex + 7) << 3) | mant);
+}
+
+static float f32_of_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* MXFP8 quantisation of n_rows rows of row_len bf16 values (row_len % 32 == 0). */
+void oracle_quant_mxfp8(const uint16_t* x, int64_t n_rows, int64_t row_len, uint8_t* codes, uint8_t* scales) {
+  const int64_t groups = row_len / 32;
+  for (int64_t r = 0; r < n_rows; ++r)
+    for (int64_t g = 0; g < groups; ++g) {
+      const uint16_t* xg = x + r * row_len + g * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)f32_of_bf16(xg[i])));
+      int sh = 0; /* log2 X */
+      if (amax > 0.0) {
+        int e;
+        (void)frexp(amax, &e);
+        sh = (e - 1) - 8;
+      }
+      scales[r * groups + g] = (uint8_t)(sh + 127);
+      for (int i = 0; i < 32; ++i)
+        codes[r * row_len + g * 32 + i] = oracle_encode_e4m3(ldexp((double)f32_of_bf16(xg[i]), -sh));
+    }
+}
+
+/* FP8 rows with one f32 scale per block: blocks of `block` elements (the last
+ * one may be shorter).  scales: [n_rows][ceil(row_len / block)]. */
+void oracle_quant_fp8_rows(const uint16_t* x, int64_t n_rows, int64_t row_len, int64_t block, uint8_t* codes,
+                           float* scales) {
+  const int64_t nb = (row_len + block - 1) / block;
+  for (int64_t r = 0; r < n_rows; ++r)
+    for (int64_t bI = 0; bI < nb; ++bI) {
+      const int64_t lo = bI * block, hi = lo + block < row_len ? lo + block : row_len;
+      float amax = 0.0f;
+      for (int64_t d = lo; d < hi; ++d) amax = fmaxf(amax, fabsf(f32_of_bf16(x[r * row_len + d])));
+      const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      scales[r * nb + bI] = sc;
+      for (int64_t d = lo; d < hi; ++d) {
+        const float qv = f32_of_bf16(x[r * row_len + d]) / sc; /* fp32 quotient */
+        codes[r * row_len + d] = oracle_encode_e4m3((double)qv);
+      }
+    }
+}

@@ -246,3 +246,107 @@ def test_attention_special_cases():
     # nothing selected -> zeros and -inf
     out, lse = oracle.sparse_attn(q, lat, -np.ones(4, np.int32), 0.1)
     assert (out == 0).all() and np.isneginf(lse).all()
+
+
+# ---------------------------------------------------------------- quantisers (cache append)
+def _all_e4m3_values():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = np.array([oracle.e4m3(int(c)) for c in codes])
+    ok = ~np.isnan(vals)
+    return codes[ok], vals[ok]
+
+
+def test_encode_e4m3_matches_torch_rounding():
+    """Every finite code round-trips; every midpoint between neighbouring
+    magnitudes and a spread of random values encode as torch's float8 cast
+    (round to nearest even) does."""
+    codes, vals = _all_e4m3_values()
+    for c, v in zip(codes, vals):
+        assert oracle.encode_e4m3(v) == c  # (code 0x80 decodes to -0.0 and encodes back to 0x80)
+    mags = np.unique(np.abs(vals))
+    mids = (mags[:-1] + mags[1:]) / 2
+    rng = np.random.default_rng(5)
+    probe = np.concatenate([mids, -mids, rng.uniform(-448, 448, 4000), rng.normal(0, 0.05, 2000),
+                            mags * (1 + 2.0 ** -12), mags * (1 - 2.0 ** -12)]).astype(np.float32)
+    probe = probe[np.abs(probe) <= 448]
+    want = torch.from_numpy(probe).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.encode_e4m3(float(v)) for v in probe], dtype=np.uint8)
+    assert (got == want).all(), probe[got != want][:5]
+
+
+def test_encode_e4m3_saturates():
+    for v in [448.0, 449.0, 464.0, 1e4, 3.4e38]:
+        assert oracle.encode_e4m3(v) == 0x7E and oracle.encode_e4m3(-v) == 0xFE
+
+
+def _bf16_bits(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).bfloat16().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_quant_mxfp8_closed_forms():
+    # integers in [-4, 4] with amax 4: X = 2^(2 - 8) = 2^-6, codes are exact
+    rng = np.random.default_rng(6)
+    ints = rng.integers(-4, 5, size=(3, 128)).astype(np.float32)
+    ints[:, 0] = 4.0
+    ints[2, 32:64] = 0.0  # an all-zero group
+    codes, scales = oracle.quant_mxfp8(_bf16_bits(ints))
+    assert scales.shape == (3, 4)
+    assert (scales[:, 0] == 127 - 6).all()
+    assert scales[2, 1] == 127 and (codes[2, 32:64] == 0).all()
+    deq = np.array([[oracle.e4m3(int(c)) for c in row] for row in codes]) * \
+        np.repeat(np.array([[oracle.e8m0(int(s)) for s in row] for row in scales]), 32, axis=1)
+    assert (deq == ints).all()
+    # amax = 1.9 * 8: X = 2^(3 - 8), the largest element needs 486.4 > 448 and saturates
+    g = np.full((1, 32), 1.0, np.float32)
+    g[0, 5] = 15.2
+    codes, scales = oracle.quant_mxfp8(_bf16_bits(g))
+    assert scales[0, 0] == 127 - 5 and codes[0, 5] == 0x7E
+    assert codes[0, 0] == oracle.encode_e4m3(32.0)
+
+
+def test_quant_mxfp8_is_nearest_code():
+    """Brute force: each code is a nearest E4M3 value to x / X (ties to even),
+    and X follows the group's amax."""
+    _, vals = _all_e4m3_values()
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((4, 64)) * np.exp(rng.uniform(-6, 6, (4, 1)))).astype(np.float32)
+    xb = _bf16_bits(x)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    codes, scales = oracle.quant_mxfp8(xb)
+    for r in range(4):
+        for g in range(2):
+            grp = xf[r, 32 * g:32 * g + 32]
+            X = oracle.e8m0(int(scales[r, g]))
+            assert X == 2.0 ** (np.floor(np.log2(np.abs(grp).max())) - 8)
+            for i in range(32):
+                t = min(abs(grp[i] / X), 448.0)
+                best = np.abs(np.abs(vals) - t).min()
+                got = abs(oracle.e4m3(int(codes[r, 32 * g + i])))
+                assert abs(got - t) == best
+
+
+def test_quant_fp8_rows_per_token_and_per_tile():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 576)).astype(np.float32)
+    x[3] = 0.0
+    xb = _bf16_bits(x)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    _, vals = _all_e4m3_values()
+    for block, nb in [(576, 1), (128, 5)]:
+        codes, scales = oracle.quant_fp8_rows(xb, block)
+        assert scales.shape == (5, nb)
+        assert (scales[3] == 1.0).all() and (codes[3] == 0).all()
+        for r in [0, 1, 4]:
+            for b in range(nb):
+                lo, hi = b * block, min(576, b * block + block)
+                seg = xf[r, lo:hi]
+                amax = np.float32(np.abs(seg).max())
+                assert scales[r, b] == np.float32(amax / np.float32(448.0))
+                # the block's largest magnitude lands on the largest code
+                j = int(np.abs(seg).argmax())
+                assert codes[r, lo + j] & 0x7F == 0x7E
+                q = (seg / scales[r, b]).astype(np.float32)
+                for i in range(0, hi - lo, 7):
+                    got = oracle.e4m3(int(codes[r, lo + i]))
+                    assert abs(abs(got) - min(abs(q[i]), 448.0)) == np.abs(np.abs(vals) - min(abs(q[i]), 448.0)).min()
+                    assert got == 0 or np.sign(got) == np.sign(q[i])
