@@ -189,7 +189,8 @@ void oracle_sparse_attn(const uint16_t* q, int64_t H, int c_fmt, const void* c, 
  *    at +-448 (OCP E4M3FN has no infinity; "satfinite");
  *  - MXFP8 (OCP Microscaling v1.0): per group of 32, shared exponent
  *    X = 2^(floor(log2 amax) - 8) (8 = the largest E4M3 exponent), stored as
- *    E8M0 code floor(log2 amax) - 8 + 127; an all-zero group takes X = 1;
+ *    E8M0 code floor(log2 amax) - 8 + 127, held to the codes 0..254 (2^-127
+ *    .. 2^127); an all-zero group takes X = 1;
  *    elements are x / X encoded as E4M3;
  *  - FP8 cache rows: f32 scale = amax / 448 of the row (or of each 128-wide
  *    tile, the fifth tile of a 576-wide latent row being 64 wide), 1 for an
@@ -249,6 +250,9 @@ void oracle_quant_mxfp8(const uint16_t* x, int64_t n_rows, int64_t row_len, uint
         (void)frexp(amax, &e);
         sh = (e - 1) - 8;
       }
+      /* E8M0 holds 2^-127 .. 2^127 (code 255 is NaN) */
+      if (sh < -127) sh = -127;
+      if (sh > 127) sh = 127;
       scales[r * groups + g] = (uint8_t)(sh + 127);
       for (int i = 0; i < 32; ++i)
         codes[r * row_len + g * 32 + i] = oracle_encode_e4m3(ldexp((double)f32_of_bf16(xg[i]), -sh));
