@@ -161,6 +161,48 @@ li_status sfa_prefill(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_le
                       int32_t top_k, float sm_scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * li_quantize_mxfp8 -- MXFP8 quantisation of bf16 rows, e.g. the indexer
+ * query before li_score_topk ("Day-0 Inference Adaptation and Optimization
+ * for Hybrid Attention Architectures", sec. 4: MXFP8 indexer query, group 32;
+ * "Optimizing Inference for Hybrid Attention LLMs", sec. 4 table).
+ *
+ *   x       [n_rows,row_len] bf16, row_len a positive multiple of 32, 16-byte aligned
+ *   codes   [n_rows,row_len] E4M3 codes out (8-byte aligned)
+ *   scales  [n_rows,row_len/32] E8M0 codes out
+ * Per group of 32 consecutive elements: X = 2^(floor(log2 amax) - 8) (E8M0
+ * code floor(log2 amax) - 8 + 127, held to 0..254; an all-zero group takes
+ * X = 1), element codes = x / X rounded to the nearest E4M3 value (ties to
+ * the even code), saturating at 448.  n_rows = 0 is a no-op.  Asynchronous
+ * on `stream`; the caller owns every buffer.
+ */
+li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+
+/*
+ * li_cache_append -- writes the new tokens' indexer-key and latent rows into
+ * the paged caches (the pages' per-step cache update before the indexer and
+ * attention read them; quantised layouts: same sections as above, FP8 KV with
+ * per-token-head-tile scales of tile 128).
+ *
+ * Token t = b*q_per_seq + j (its request's j-th new token) is written at
+ * position L_b - q_per_seq + j: page block_table[b][pos/64], slot pos%64.
+ * Tokens whose position falls outside [0, max_pages*64) are skipped.
+ *   k_new     [T,128] bf16 indexer-key rows, or NULL (no key cache update)
+ *   k_dtype   LI_BF16 (copied) or LI_FP8 (codes; k_scales[page][slot] = amax/448
+ *             of the row, 1 for an all-zero row; codes = fl32(x/scale) to the
+ *             nearest E4M3, ties to even, saturating)
+ *   kv_new    [T,576] bf16 latent rows (512 latent + 64 rope), or NULL
+ *   kv_dtype  LI_BF16 or LI_FP8 with kv_scale_groups 1 (one scale per row) or 5
+ *             (one per 128-wide tile, the fifth 64 wide); scales as for the key
+ * Caches and scales as in li_score_topk / sfa_decode.  Asynchronous on
+ * `stream`; rows of other positions are left untouched.
+ */
+li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                          int32_t max_pages, int32_t num_pages, const void* k_new, int32_t k_dtype, void* k_cache,
+                          float* k_scales, const void* kv_new, int32_t kv_dtype, void* kv_cache, float* kv_scales,
+                          int32_t kv_scale_groups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LiError",
-           "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero"]
+           "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
+           "li_cache_append"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_li.so")
@@ -27,7 +28,7 @@ LI_OK = 0
 _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKSPACE", -4: "LI_ERR_HIP"}
 
 EXPORTS = ["li_version", "li_last_error", "li_score_topk_workspace_size", "li_workspace_zero", "li_score_topk",
-           "sfa_workspace_size", "sfa_decode", "sfa_prefill"]
+           "sfa_workspace_size", "sfa_decode", "sfa_prefill", "li_quantize_mxfp8", "li_cache_append"]
 
 
 class LiError(RuntimeError):
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.sfa_decode.argtypes = sfa_args
         L.sfa_prefill.restype = i32
         L.sfa_prefill.argtypes = sfa_args
+        L.li_quantize_mxfp8.restype = i32
+        L.li_quantize_mxfp8.argtypes = [i32, i32, vp, vp, vp, vp]
+        L.li_cache_append.restype = i32
+        L.li_cache_append.argtypes = [i32, i32, vp, vp, i32, i32, vp, i32, vp, vp, vp, i32, vp, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -176,3 +181,40 @@ def sfa_decode(q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None
 def sfa_prefill(q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None, **kw):
     """sfa_decode's operation with the launch shape for a prefill chunk."""
     return _sfa(lib().sfa_prefill, q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales, **kw)
+
+
+def li_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                      stream=None):
+    """MXFP8 quantisation of bf16 x [..., L] (L % 32 == 0): returns (codes uint8
+    [..., L] E4M3, scales uint8 [..., L/32] E8M0)."""
+    L = x.shape[-1]
+    n = x.numel() // L if L else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], L // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().li_quantize_mxfp8(n, L, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def li_cache_append(seq_lens: torch.Tensor, block_table: torch.Tensor, k_new: torch.Tensor | None = None,
+                    k_cache: torch.Tensor | None = None, kv_new: torch.Tensor | None = None,
+                    kv_cache: torch.Tensor | None = None, k_scales: torch.Tensor | None = None,
+                    kv_scales: torch.Tensor | None = None, stream=None):
+    """Writes the new tokens' rows into the paged caches.  k_new [T,128] bf16 into
+    k_cache [NP,64,128] (bf16, or uint8 codes with k_scales [NP,64] f32); kv_new
+    [T,576] bf16 into kv_cache [NP,64,576] (bf16, or uint8 codes with kv_scales
+    [NP,64,G] f32, G = 1 or 5).  Token t of request b goes to position
+    seq_lens[b] - n_q + (t % n_q)."""
+    B = seq_lens.shape[0]
+    ref = k_new if k_new is not None else kv_new
+    T = ref.shape[0]
+    if T % B:
+        raise ValueError("the number of new rows must be a multiple of len(seq_lens)")
+    pool = k_cache if k_cache is not None else kv_cache
+    groups = 1 if kv_scales is None else (kv_scales.shape[2] if kv_scales.dim() == 3 else 1)
+    st = lib().li_cache_append(B, T // B, _ptr(seq_lens), _ptr(block_table), block_table.shape[1], pool.shape[0],
+                               _ptr(k_new), LI_BF16 if k_cache is None else _dtype_of(k_cache), _ptr(k_cache),
+                               _ptr(k_scales), _ptr(kv_new), LI_BF16 if kv_cache is None else _dtype_of(kv_cache),
+                               _ptr(kv_cache), _ptr(kv_scales), groups, _stream(stream))
+    _check(st)

@@ -303,4 +303,70 @@ li_status sfa_prefill(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_le
                     kv_scales, kv_scale_groups, idx, top_k, sm_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  if (n_rows < 0) return fail(LI_ERR_INVALID_ARG, "n_rows must not be negative (got %d)", n_rows);
+  if (row_len <= 0 || row_len % 32 != 0)
+    return fail(LI_ERR_INVALID_ARG, "row_len must be a positive multiple of 32 (got %d)", row_len);
+  if (n_rows == 0) return LI_OK;
+  if (!x || !codes || !scales) return fail(LI_ERR_INVALID_ARG, "x, codes and scales must not be NULL");
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0)
+    return fail(LI_ERR_INVALID_ARG, "x must be 16-byte aligned and codes 8-byte aligned");
+  sli::QuantArgs a;
+  a.n_rows = n_rows;
+  a.row_len = row_len;
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  hipError_t e = sli::launch_mxfp8_quant(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LI_OK : hip_fail(e, "MXFP8 quantisation launch");
+}
+
+li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                          int32_t max_pages, int32_t num_pages, const void* k_new, int32_t k_dtype, void* k_cache,
+                          float* k_scales, const void* kv_new, int32_t kv_dtype, void* kv_cache, float* kv_scales,
+                          int32_t kv_scale_groups, void* stream) {
+  li_status st = check_paged(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages);
+  if (st != LI_OK) return st;
+  if (!k_new && !kv_new) return fail(LI_ERR_INVALID_ARG, "k_new and kv_new must not both be NULL");
+  sli::AppendArgs a;
+  a.B = num_seqs;
+  a.n_q = q_per_seq;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.k_new = k_new;
+  a.k_fp8 = false;
+  a.k_cache = k_cache;
+  a.k_scales = k_scales;
+  a.kv_new = kv_new;
+  a.kv_fp8 = false;
+  a.kv_groups = 1;
+  a.kv_cache = kv_cache;
+  a.kv_scales = kv_scales;
+  if (k_new) {
+    if (k_dtype != LI_BF16 && k_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown k_dtype %d", k_dtype);
+    a.k_fp8 = k_dtype == LI_FP8;
+    if (!k_cache) return fail(LI_ERR_INVALID_ARG, "k_cache must not be NULL when k_new is given");
+    if (a.k_fp8 && !k_scales) return fail(LI_ERR_INVALID_ARG, "an FP8 key cache needs k_scales");
+    if (!aligned16(k_new) || !aligned16(k_cache)) return fail(LI_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
+  }
+  if (kv_new) {
+    if (kv_dtype != LI_BF16 && kv_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+    a.kv_fp8 = kv_dtype == LI_FP8;
+    if (!kv_cache) return fail(LI_ERR_INVALID_ARG, "kv_cache must not be NULL when kv_new is given");
+    if (a.kv_fp8) {
+      if (!kv_scales) return fail(LI_ERR_INVALID_ARG, "an FP8 latent cache needs kv_scales");
+      if (kv_scale_groups != 1 && kv_scale_groups != 5)
+        return fail(LI_ERR_UNSUPPORTED, "kv_scale_groups must be 1 (per row) or 5 (per 128-wide tile), got %d",
+                    kv_scale_groups);
+      a.kv_groups = kv_scale_groups;
+    }
+    if (!aligned16(kv_new) || !aligned16(kv_cache)) return fail(LI_ERR_INVALID_ARG, "kv_new and kv_cache must be 16-byte aligned");
+  }
+  hipError_t e = sli::launch_cache_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LI_OK : hip_fail(e, "cache append launch");
+}
+
 }  // extern "C"

@@ -57,6 +57,31 @@ struct SfaArgs {
   float* part_ml;  // [T][n_splits][H][2]   (running max in log2 units, sum)
 };
 
+struct QuantArgs {
+  int n_rows, row_len;  // row_len % 32 == 0
+  const void* x;        // bf16 [n_rows][row_len]
+  uint8_t* codes;       // [n_rows][row_len] E4M3
+  uint8_t* scales;      // [n_rows][row_len / 32] E8M0
+};
+
+struct AppendArgs {
+  int B, n_q, max_pages, num_pages;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const void* k_new;  // bf16 [T][128] or null
+  bool k_fp8;
+  void* k_cache;      // [num_pages][64][128] bf16 or E4M3
+  float* k_scales;    // [num_pages][64] (FP8)
+  const void* kv_new; // bf16 [T][576] or null
+  bool kv_fp8;
+  int kv_groups;      // 1 or 5 (FP8)
+  void* kv_cache;     // [num_pages][64][576] bf16 or E4M3
+  float* kv_scales;   // [num_pages][64][kv_groups] (FP8)
+};
+
+hipError_t launch_mxfp8_quant(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_cache_append(const AppendArgs& a, hipStream_t stream);
+
 int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus);
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);

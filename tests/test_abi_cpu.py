@@ -78,3 +78,45 @@ def test_workspace_sizes():
     b = li.li_score_topk_workspace_size(32, 2, 512, 2048)
     assert 0 < a < b
     assert li.sfa_workspace_size(32, 128, 2048) > 0
+
+
+def _call_quant(**over):
+    L = li.lib()
+    P = ctypes.c_void_p(0x10000)
+    args = dict(n_rows=4, row_len=128, x=P, codes=P, scales=P, stream=None)
+    args.update(over)
+    return L.li_quantize_mxfp8(*args.values()), L.li_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(row_len=100), -1), (dict(row_len=0), -1), (dict(n_rows=-1), -1), (dict(x=None), -1),
+    (dict(scales=None), -1), (dict(x=ctypes.c_void_p(0x10008)), -1), (dict(codes=ctypes.c_void_p(0x10004)), -1),
+])
+def test_quantize_argument_errors(over, status):
+    st, msg = _call_quant(**over)
+    assert st == status and msg
+
+
+def test_quantize_zero_rows_is_a_no_op():
+    st, _ = _call_quant(n_rows=0, x=None, codes=None, scales=None)
+    assert st == 0
+
+
+def _call_append(**over):
+    L = li.lib()
+    P = ctypes.c_void_p(0x10000)
+    args = dict(num_seqs=2, q_per_seq=1, seq_lens=P, bt=P, max_pages=32, num_pages=64, k_new=P, k_dtype=0, k_cache=P,
+                k_scales=None, kv_new=P, kv_dtype=0, kv_cache=P, kv_scales=None, groups=1, stream=None)
+    args.update(over)
+    return L.li_cache_append(*args.values()), L.li_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k_new=None, kv_new=None), -1), (dict(num_seqs=0), -1), (dict(seq_lens=None), -1),
+    (dict(k_dtype=4), -2), (dict(k_dtype=1), -1), (dict(k_cache=None), -1), (dict(kv_dtype=1), -1),
+    (dict(kv_dtype=1, kv_scales=ctypes.c_void_p(0x10000), groups=3), -2), (dict(kv_cache=None), -1),
+    (dict(k_new=ctypes.c_void_p(0x10008)), -1), (dict(kv_cache=ctypes.c_void_p(0x10004)), -1),
+])
+def test_cache_append_argument_errors(over, status):
+    st, msg = _call_append(**over)
+    assert st == status and msg

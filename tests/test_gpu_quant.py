@@ -1,0 +1,99 @@
+"""GPU parity of the cache append and the quantisers (through the C ABI)
+against the CPU oracle on the same seeded inputs: codes, scales and the
+written cache bytes must match bit for bit, and rows of other positions must
+be left untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def li(gpu_ready):
+    import sparse_attention_li_amd as li
+    li.lib()
+    return li
+
+
+def _bf16(a):
+    """float32 array -> (bf16 bits as uint16, the same bits as a device int16 tensor)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).bfloat16()
+    return t.view(torch.int16).numpy().view(np.uint16), t.view(torch.int16).cuda()
+
+
+def test_mxfp8_matches_oracle(li):
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((7 * 64, 128)).astype(np.float32) * np.exp(rng.uniform(-8, 8, (7 * 64, 1)))
+    x[3, 32:64] = 0.0                      # an all-zero group
+    x[5, 0:32] = rng.integers(-4, 5, 32)   # integers, amax <= 4
+    x[9, 64:96] = 1.0
+    x[9, 70] = 15.2                        # largest element saturates at 448
+    bits, xt = _bf16(x)
+    codes, scales = li.li_quantize_mxfp8(xt.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant_mxfp8(bits)
+    assert (scales.cpu().numpy() == rs).all()
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:3]}: gpu {got[tuple(bad[0])]} oracle {rc[tuple(bad[0])]}"
+
+
+def _pools(rng, num_pages, fp8_k, fp8_kv, groups):
+    k = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 256), dtype=np.uint8)).cuda()
+    kv = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 1152), dtype=np.uint8)).cuda()
+    k_pool = k[:, :, :128].contiguous() if fp8_k else k.view(torch.int16)
+    kv_pool = kv[:, :, :576].contiguous() if fp8_kv else kv.view(torch.int16)
+    ks = torch.from_numpy(rng.uniform(1, 2, (num_pages, 64)).astype(np.float32)).cuda() if fp8_k else None
+    kvs = torch.from_numpy(rng.uniform(1, 2, (num_pages, 64, groups)).astype(np.float32)).cuda() if fp8_kv else None
+    return k_pool, kv_pool, ks, kvs
+
+
+@pytest.mark.parametrize("fp8_k,fp8_kv,groups,n_q", [
+    (False, False, 1, 1), (True, True, 1, 1), (True, True, 5, 2), (False, True, 5, 1), (True, False, 1, 2),
+])
+def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
+    rng = np.random.default_rng(40 + 2 * groups + n_q + 4 * fp8_k)
+    B, max_pages, num_pages = 5, 6, 40
+    seq_lens = np.array([1, 64, 65, 200, 384][:B], dtype=np.int32)   # (L = 1 with two new tokens: one has no slot)
+    bt = np.stack([rng.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
+    T = B * n_q
+    k_new = rng.standard_normal((T, 128)).astype(np.float32) * np.exp(rng.uniform(-3, 3, (T, 1)))
+    kv_new = rng.standard_normal((T, 576)).astype(np.float32) * np.exp(rng.uniform(-3, 3, (T, 1)))
+    kv_new[min(2, T - 1), 128:256] = 0.0  # an all-zero tile
+    kb, kt = _bf16(k_new)
+    vb, vt = _bf16(kv_new)
+    k_pool, kv_pool, ks, kvs = _pools(rng, num_pages, fp8_k, fp8_kv, groups)
+    before = [t.clone() if t is not None else None for t in (k_pool, kv_pool, ks, kvs)]
+    li.li_cache_append(torch.from_numpy(seq_lens).cuda(), torch.from_numpy(bt).cuda(), k_new=kt.view(torch.bfloat16),
+                       k_cache=k_pool, kv_new=vt.view(torch.bfloat16), kv_cache=kv_pool, k_scales=ks, kv_scales=kvs)
+    torch.cuda.synchronize()
+    # expected: the pools before, with each token's row replaced
+    exp = [t.cpu().numpy().copy() if t is not None else None for t in before]
+    if fp8_k:
+        kc, ksc = oracle.quant_fp8_rows(kb, 128)
+    if fp8_kv:
+        vc, vsc = oracle.quant_fp8_rows(vb, 128 if groups == 5 else 576)
+    for t in range(T):
+        b, j = divmod(t, n_q)
+        pos = int(seq_lens[b]) - n_q + j
+        if pos < 0:
+            continue
+        pg, sl = bt[b, pos // 64], pos % 64
+        if fp8_k:
+            exp[0][pg, sl] = kc[t]
+            exp[2][pg, sl] = ksc[t, 0]
+        else:
+            exp[0][pg, sl] = kb[t].view(np.int16)
+        if fp8_kv:
+            exp[1][pg, sl] = vc[t]
+            exp[3][pg, sl] = vsc[t]
+        else:
+            exp[1][pg, sl] = vb[t].view(np.int16)
+    for got, want, name in zip((k_pool, kv_pool, ks, kvs), exp, ("k_cache", "kv_cache", "k_scales", "kv_scales")):
+        if got is None:
+            continue
+        g = got.cpu().numpy()
+        assert np.array_equal(g.view(np.uint8), want.view(np.uint8)), f"{name}: {int((g != want).sum())} mismatches"
