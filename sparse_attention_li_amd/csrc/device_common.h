@@ -164,6 +164,74 @@ __device__ uint32_t block_radix_select(Get get, int N, int k, uint32_t* s_hist, 
   return prefix;
 }
 
+// The same selection by a single wave for N <= 64*PER keys (every lane of the
+// wave calls it; no block barrier): one LDS histogram of 256 words per 8-bit
+// window, private to the wave, updated with atomics and read back in order
+// (a wave's LDS operations complete in order).  On return every lane holds
+// tau and n_greater.
+template <int PER, class Get>
+__device__ uint32_t wave_radix_select(Get get, int N, int k, uint32_t* s_hist, int& n_greater) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t key[PER];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int i = lane + r * kWave;
+    key[r] = i < N ? get(i) : 0u;
+    if (i < N) {
+      lo = key[r] < lo ? key[r] : lo;
+      hi = key[r] > hi ? key[r] : hi;
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lo == hi) {
+    n_greater = 0;
+    return lo;
+  }
+  int top = 31 - __clz(lo ^ hi);
+  uint32_t prefix = lo & ~((2u << top) - 1u);
+  uint32_t remaining = (uint32_t)k;
+  while (top >= 0) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const int width = top - shift + 1;
+    const uint32_t above = top == 31 ? 0u : ~((2u << top) - 1u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_hist[4 * lane + i] = 0u;
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+      if (lane + r * kWave < N && (key[r] & above) == prefix)
+        atomicAdd(&s_hist[(key[r] >> shift) & ((1u << width) - 1u)], 1u);
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = s_hist[255 - 4 * lane - i];
+    const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t excl = incl - sum;
+    const bool mine = excl < remaining && remaining <= incl;
+    uint32_t dsel = 0, rsel = 0;
+    if (mine) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (acc < remaining && remaining <= acc + h[i]) {
+          dsel = 255u - 4u * lane - i;
+          rsel = remaining - acc;
+        }
+        acc += h[i];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;  // exactly one lane
+    dsel = __shfl(dsel, src, kWave);
+    rsel = __shfl(rsel, src, kWave);
+    prefix |= dsel << shift;
+    remaining = rsel;
+    top = shift - 1;
+  }
+  n_greater = k - (int)remaining;
+  return prefix;
+}
+
 // The same selection for inputs too large to hold in registers (rare
 // fallback paths): four 8-bit passes, each streaming all N keys through get().
 template <class Get>

@@ -637,8 +637,24 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
       return (uint32_t)xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
     };
     int ngt;
-    const uint32_t tau = in_lds ? block_radix_select<kBandCap / THREADS>(key_at, (int)NB, need, sm.hist, sm.sel, ngt)
-                                : block_radix_select_big(key_at, (int)NB, need, sm.hist, sm.sel, ngt);
+    uint32_t tau;
+    if (in_lds && NB <= 8u * kWave) {
+      // the usual band (a few hundred entries): one wave selects, no block barriers
+      if (wid == 0) {
+        int g;
+        const uint32_t tv = wave_radix_select<8>([&](int f) { return s_bk[f]; }, (int)NB, need, sm.hist, g);
+        if (lane == 0) {
+          sm.sel[2] = tv;
+          sm.sel[3] = (uint32_t)g;
+        }
+      }
+      __syncthreads();
+      tau = sm.sel[2];
+      ngt = (int)sm.sel[3];
+    } else {
+      tau = in_lds ? block_radix_select<kBandCap / THREADS>(key_at, (int)NB, need, sm.hist, sm.sel, ngt)
+                   : block_radix_select_big(key_at, (int)NB, need, sm.hist, sm.sel, ngt);
+    }
     const uint32_t ties = (uint32_t)(need - ngt);  // keys equal to tau that are taken, lowest positions first
     int32_t* out = a.idx_out + tok * K;
 
