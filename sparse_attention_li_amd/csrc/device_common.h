@@ -80,6 +80,33 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp,
   return off + incl - v;
 }
 
+// Two exclusive scans with one pair of barriers.  s_tmp needs 2*blockDim.x/64
+// entries.  Returns the exclusive prefix of a; b's goes to pre_b; both totals
+// to every thread.
+__device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uint32_t* s_tmp, uint32_t& tot_a,
+                                                     uint32_t& pre_b, uint32_t& tot_b) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == kWave - 1) {
+    s_tmp[wid] = ia;
+    s_tmp[nw + wid] = ib;
+  }
+  __syncthreads();
+  uint32_t oa = 0, ta = 0, ob = 0, tb = 0;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t xa = s_tmp[i], xb = s_tmp[nw + i];
+    oa += (i < wid) ? xa : 0u;
+    ta += xa;
+    ob += (i < wid) ? xb : 0u;
+    tb += xb;
+  }
+  __syncthreads();
+  tot_a = ta;
+  tot_b = tb;
+  pre_b = ob + ib - b;
+  return oa + ia - a;
+}
+
 // ---------------------------------------------------------------- radix select
 // Finds the k-th largest key (1 <= k <= N) among N <= PER*blockDim.x keys
 // given by get(i) (any values, 0 included).  On return every thread

@@ -666,35 +666,31 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
         gt += key > tau ? 1u : 0u;
         eq += key == tau ? 1u : 0u;
       }
-      uint32_t gt_before, eq_before;
-      block_excl_scan(gt | (eq << 16), sm.scan, gt_before);  // both <= band size < 2^16
-      eq_before = gt_before >> 16;
-      gt_before &= 0xffffu;
-      const uint32_t off = sm.abase[c] + gt_before + min(ties, eq_before);
-      // own keys in position order
-      uint32_t kk[PER], nt = 0;
+      // own keys in position order: selected for certain (>= hi, or in the
+      // band and > tau) or tied at tau
+      uint32_t kk[PER], nd = 0, nt = 0;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         kk[i] = s_keys[j * CHUNK + tid * PER + i];
-        nt += (kk[i] == tau && kk[i] >= lo_ref[j] && kk[i] < hi_ref[j]) ? 1u : 0u;
+        const bool band = kk[i] >= lo_ref[j] && kk[i] < hi_ref[j];
+        nd += (kk[i] >= hi_ref[j] || (band && kk[i] > tau)) ? 1u : 0u;
+        nt += (band && kk[i] == tau) ? 1u : 0u;
       }
-      uint32_t tt;
-      uint32_t tr = eq_before + block_excl_scan(nt, sm.scan, tt);
-      bool selv[PER];
-      uint32_t ns = 0;
+      // one scan: totals of the earlier chunks' band, prefixes of this chunk's
+      // keys (every count <= the band or the chunk, < 2^16)
+      uint32_t before, pre, tot_pre;
+      block_excl_scan2(gt | (eq << 16), nd | (nt << 16), sm.scan, before, pre, tot_pre);
+      const uint32_t gt_before = before & 0xffffu, eq_before = before >> 16;
+      const uint32_t avail = ties > eq_before ? ties - eq_before : 0u;  // ties left for this chunk
+      uint32_t tr = pre >> 16;                                            // ties of this chunk before my keys
+      uint32_t o = sm.abase[c] + gt_before + min(ties, eq_before) + (pre & 0xffffu) + min(avail, tr);
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const bool band = kk[i] >= lo_ref[j] && kk[i] < hi_ref[j];
         const bool tie = band && kk[i] == tau;
-        selv[i] = kk[i] >= hi_ref[j] || (band && (kk[i] > tau || (tie && tr < ties)));
+        if (kk[i] >= hi_ref[j] || (band && kk[i] > tau) || (tie && tr < avail)) out[o++] = s0 + tid * PER + i;
         tr += tie ? 1u : 0u;
-        ns += selv[i] ? 1u : 0u;
       }
-      uint32_t nst;
-      uint32_t o = off + block_excl_scan(ns, sm.scan, nst);
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (selv[i]) out[o++] = s0 + tid * PER + i;
     } else {
       // kModeFull: the whole request, chunk by chunk, from the published
       // lists (keys >= hi all taken; band entries by tau and tie rank)
