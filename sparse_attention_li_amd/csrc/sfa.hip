@@ -30,6 +30,9 @@
 // When a token's index row is split over several workgroups, each writes an
 // unnormalised fp32 partial and (max, sum) per head, and a combine kernel
 // merges them.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -382,12 +385,63 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 latent rows, every head of the token in one workgroup.
 //
-// Wave w owns heads 32w .. 32w+31 from end to end: the full 576-wide logits
-// (its q^T operands, 144 VGPRs, stay resident) and all 512 output columns (16
-// accumulator tiles), so the waves share only the gathered tile and each
-// selected row crosses the memory system once per slice.  Tiles move through
-// a four-slot LDS ring, so three tiles are in flight while one is consumed
-// (logits on two independent MFMA chains, online softmax, output product).
+// Wave w computes the full 576-wide logits and the online softmax of heads
+// 32w .. 32w+31 (its q^T operands, 144 VGPRs, stay resident), and the output
+// of all the heads for latent columns 128w .. 128w+127 (16 accumulator tiles):
+// a wave reads a quarter of each tile transposed, instead of all of it, and
+// the softmax weights of every head reach every wave through an 8 KiB LDS
+// buffer, laid out as the output MFMA's operand registers.  Each selected row
+// crosses the memory system once per slice.  Tiles move through a four-slot
+// LDS ring: two tiles are in flight while two are consumed (the logits of one,
+// the output product of the one before).
+// Read schedule of the bf16 kernel's output product (32 MFMAs per tile and
+// wave; MFMA j uses k-block kk = j / 16, column tile mm = (j / 4) % 4 and head
+// block hb = j % 4, i.e. transposed pair pi = 4 kk + mm and weights
+// P(kk, hb)).  LDS reads in issue order: P(0, 0..3), pairs 0 .. A-1; pair
+// pi + A just before the first MFMA of pair pi; P(1, hb) just after the last
+// MFMA that uses P(0, hb).  LDS reads of one wave complete in order, so MFMA
+// j waits until no more than issued - needed of them are outstanding.
+// reads issued before MFMA j's wait (its own pair issue included)
+__host__ __device__ constexpr int sfa_pv_issued(int ahead, int j) {
+  int cnt = 4 + 2 * ahead;
+  for (int i = 0; i <= j; ++i) {
+    const int kk = i >> 4, mm = (i >> 2) & 3, pi = 4 * kk + mm;
+    if ((i & 3) == 0 && pi + ahead < 8) cnt += 2;
+    if (i < j && kk == 0 && mm == 3) cnt += 1;
+  }
+  return cnt;
+}
+// one past the issue index of the last read MFMA j needs
+__host__ __device__ constexpr int sfa_pv_needed(int ahead, int j) {
+  const int kk = j >> 4, mm = (j >> 2) & 3, hb = j & 3, pi = 4 * kk + mm;
+  const int p_at = kk == 0 ? hb : sfa_pv_issued(ahead, 12 + hb);
+  const int pair_last = pi < ahead ? 5 + 2 * pi : sfa_pv_issued(ahead, 4 * (pi - ahead)) - 1;
+  return (p_at > pair_last ? p_at : pair_last) + 1;
+}
+__host__ __device__ constexpr int sfa_pv_outstanding(int ahead, int j) {
+  return sfa_pv_issued(ahead, j) - sfa_pv_needed(ahead, j);
+}
+__host__ __device__ constexpr bool sfa_pv_schedule_ok(int ahead) {
+  for (int j = 0; j < 32; ++j) {
+    const int w = sfa_pv_outstanding(ahead, j);
+    if (w < 0 || w > 8) return false;
+  }
+  return sfa_pv_outstanding(ahead, 31) == 0;  // everything awaited by the last MFMA
+}
+constexpr int kPvAhead = 1;  // transposed pairs read ahead of their first MFMA
+static_assert(sfa_pv_schedule_ok(1) && sfa_pv_schedule_ok(2), "output-product read schedule");
+
+// Calls f(std::integral_constant<int, J>) for J = 0 .. N-1: the body is
+// instantiated once per J, so everything indexed by J is a constant.
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 #ifndef SLI_NO_PINS
 #define SLI_PIN_V(x) asm volatile("" : "+v"(x))
 #define SLI_PIN_A(x) asm volatile("" : "+a"(x))
@@ -402,12 +456,12 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
   constexpr int MI = 16;        // 32-column output tiles
   constexpr int PVS = 2 * MI;   // output MFMAs per tile
   constexpr int DPW = 36 / NW;  // direct-to-LDS loads per wave per tile
-  constexpr int PD = 2;         // transposed-read pairs issued this many steps ahead
   constexpr int PDL = 4;        // logit operand reads issued this many steps ahead
   static_assert(36 % NW == 0, "the 36 loads of a tile are dealt evenly over the waves");
   static_assert(2 * DPW <= 63, "two tiles of loads in flight per wave");
-  static_assert(DPW <= PVS, "a wave's loads of a tile fit between the output MFMAs");
-  static_assert(PD <= 4 && PDL <= 4, "explicit LDS-read waits cover at most 4 steps in flight");
+  static_assert(3 * DPW <= PVS, "a wave's loads of a tile fit between the output MFMAs");
+  static_assert(PDL <= 4, "explicit LDS-read waits cover at most 4 steps in flight");
+  static_assert(NW == 4, "four head blocks and four column quarters");
   // four ring slots as separate LDS objects: the compiler can then tell a read
   // of one slot from a direct-to-LDS load into another and does not make the
   // read wait for every load in flight
@@ -415,8 +469,15 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
   __shared__ __attribute__((aligned(128))) char slot1[kTileBytes];
   __shared__ __attribute__((aligned(128))) char slot2[kTileBytes];
   __shared__ __attribute__((aligned(128))) char slot3[kTileBytes];
+  // P^T operands of one tile for every head: 16 bytes per (head block, k-block, lane)
+  __shared__ __attribute__((aligned(128))) char pbuf[NW * 2 * 64 * 16];
   __shared__ int rows[kMaxSplitRows];
-  __shared__ int s_fallback;
+  // The last 4 KiB of a slot hold the tile's rope columns, read only by the
+  // logits; once every wave is past them they carry the tile's softmax
+  // rescale factors (128 floats at +0, one flag per head block at +512).  The
+  // prologue's minimum row sits there in slot 3 (no tile has been loaded yet).
+  constexpr int kRope = 32768;
+  int* const s_fallback = reinterpret_cast<int*>(slot3 + kRope);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 31, half = lane >> 5, gi = lane & 15;
 
@@ -443,7 +504,7 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
   // The index entries and then the page ids are loaded (two dependent memory
   // latencies); the q loads are issued while the page ids are in flight, so
   // they overlap with the rows' resolution and with the first tiles' loads.
-  if (tid == 0) s_fallback = 0x7fffffff;
+  if (tid == 0) *s_fallback = 0x7fffffff;
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   constexpr int RPT = kMaxSplitRows / NT;  // rows per thread: one pass covers any slice
@@ -490,11 +551,11 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
         if (valid) fb = min(fb, rr);
       }
     }
-    if (fb != 0x7fffffff) atomicMin(&s_fallback, fb);
+    if (fb != 0x7fffffff) atomicMin(s_fallback, fb);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
-  const int fallback = __builtin_amdgcn_readfirstlane(s_fallback);  // uniform: kept in a scalar register
+  const int fallback = __builtin_amdgcn_readfirstlane(*s_fallback);  // uniform: kept in a scalar register
   const int tiles = fallback != 0x7fffffff ? n_tiles : 0;
   // row read in place of skipped entries (and by the prologue's loads past
   // the last tile): a valid row of the slice, else the pool's first row
@@ -516,60 +577,84 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) pr[r] = rows[tile * kTileRows + 8 * (wid + NW * r) + (lane >> 3)];
   };
-  // load k of this wave for `tile` (tile < tiles unless it is a prologue load)
-  auto load_one = [&](int tile, const int (&pr)[4], int k) {
-    const int i = wid + NW * k;  // (i % 4) = wid + NW (k % RPW), i / 4 = k / RPW
-    const int r = RPW == 1 ? pr[0] : RPW == 2 ? ((k & 1) ? pr[1] : pr[0]) : pr[k & 3];
-    const int row = (r >= 0 && tile < tiles) ? r : fb_row;
-    const char* src = static_cast<const char*>(a.kv) + ((size_t)row * 72 + c_lane) * 16 + 128 * (k / RPW);
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(ring(tile) + 1024 * i), 16, 0, 0);
+  // With four waves a lane copies one row per tile (tile < tiles unless it
+  // is a prologue load).  The loads go through a buffer resource over the
+  // pool with one 1152-byte record per latent row: the row is the index, the
+  // lane's chunk the per-lane offset and load k's 128-byte step the
+  // wave-uniform offset, so a load costs no per-lane address arithmetic.
+  static_assert(RPW == 1, "one row per lane and tile");
+  const uint32_t pool_rows = (uint32_t)min((long long)a.num_pages * 64, 0xffffffffll);
+  const auto kv_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kv), (short)1152, (int)pool_rows, 0x00020000);
+  const uint32_t c16 = 16 * c_lane;
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+  auto tile_row = [&](int tile, const int (&pr)[4]) -> int { return (pr[0] >= 0 && tile < tiles) ? pr[0] : fb_row; };
+  // load k of this wave into the tile at dst (= its slot + 1 KiB x wave)
+  auto load_one = [&](char* dst, int row, int k) {
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + 1024 * NW * k), 16, row, c16, 128 * k, 0, 0);
   };
   auto issue = [&](int tile) {
     int pr[4];
     tile_rows(tile, pr);
+    const int row = tile_row(tile, pr);
+    char* dst = ring(tile) + 1024 * wid_s;
 #pragma unroll
-    for (int k = 0; k < DPW; ++k) load_one(tile, pr, k);
+    for (int k = 0; k < DPW; ++k) load_one(dst, row, k);
   };
 
   // ---------------------------------------------------------------- operand reads
   // Byte offsets inside a tile (tile_off with the swizzle resolved per lane):
   // logits k-step k of lane (n, half) = row n, chunk 2k + half
-  //   = abase[k % 4] + 4096 (k / 4);
-  // output product j (k-block kk = j / 16, column tile m = j % 16): the
-  // 16-lane group reads rows r0..r0+3 and r0+8..r0+11 (r0 = 16 kk + tr_row)
-  // of two adjacent chunks, lane gi receiving one column, four consecutive
-  // rows per read; the low read sits at pbase[m % 2] + 4096 (m / 2) + 2048 kk
-  // and the high one 1024 bytes further.
-  int abase[4], pbase[2];
+  //   = (abase ^ 32 (k % 4)) + 4096 (k / 4);
+  // output column tile m (32 columns) at k-block kk: the 16-lane group reads
+  // rows r0..r0+3 and r0+8..r0+11 (r0 = 16 kk + tr_row) of two adjacent
+  // chunks, lane gi receiving one column, four consecutive rows per read; the
+  // low read sits at (pbase ^ 64 (m % 2)) + 4096 (m / 2) + 2048 kk and the
+  // high one 1024 bytes further.  This wave's column tiles are
+  // m = 4 wid .. 4 wid + 3.  (The swizzle only permutes chunks inside an
+  // aligned group of 8 or 4, so the per-step offsets are XORs of one base;
+  // slot bases are multiples of 128 and keep those bits clear.)
+  int abase, pbase;
   {
     const int tr_row = 4 * half + (gi >> 2);
     const int tr_chunk = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) abase[j] = 16 * (64 * (n >> 3) + 8 * (n & 7) + ((2 * j + half) ^ swz(n)));
-#pragma unroll
-    for (int j = 0; j < 2; ++j) pbase[j] = 16 * (8 * tr_row + ((4 * j + tr_chunk) ^ swz(tr_row))) + 8 * (gi & 1);
+    abase = 16 * (64 * (n >> 3) + 8 * (n & 7) + (half ^ swz(n)));
+    pbase = 16 * (8 * tr_row + (tr_chunk ^ swz(tr_row))) + 8 * (gi & 1);
   }
-  // The transposed reads are issued as instructions of their own: the wait
-  // pass cannot tell the intrinsic's LDS read from the direct-to-LDS loads in
-  // flight into other slots and would drain them all first.  Their results
-  // are awaited explicitly (tr_wait) before use.
+  // The LDS operand reads are issued as instructions of their own: the wait
+  // pass cannot tell an LDS read from the direct-to-LDS loads in flight into
+  // other slots and would drain them all first.  Their results are awaited
+  // explicitly before use.
   auto lds_addr = [](const char* p) -> uint32_t { return (uint32_t)(uintptr_t)(const lds_void*)p; };
-  auto pv_issue = [&](uint32_t c, int j, bf16x4& lo, bf16x4& hi) {
-    const int kk = j / MI, m = j % MI;
-    const uint32_t p = c + pbase[m & 1];
-    switch (4096 * (m >> 1) + 2048 * kk) {
+  // transposed pair of this wave's column tile mm (0..3) at k-block kk
+  auto pv_issue = [&](uint32_t c, int kk, int mm, bf16x4& lo, bf16x4& hi) {
+    const uint32_t p = (c + pbase) ^ (64 * (mm & 1));
+    switch (4096 * (mm >> 1) + 2048 * kk) {
 #define SLI_TR_CASE(OFF)                                                                   \
   case OFF:                                                                                \
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(p), "i"(OFF));     \
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(p), "i"(OFF + 1024)); \
     break;
       SLI_TR_CASE(0) SLI_TR_CASE(2048) SLI_TR_CASE(4096) SLI_TR_CASE(6144)
-      SLI_TR_CASE(8192) SLI_TR_CASE(10240) SLI_TR_CASE(12288) SLI_TR_CASE(14336)
-      SLI_TR_CASE(16384) SLI_TR_CASE(18432) SLI_TR_CASE(20480) SLI_TR_CASE(22528)
-      SLI_TR_CASE(24576) SLI_TR_CASE(26624) SLI_TR_CASE(28672) SLI_TR_CASE(30720)
 #undef SLI_TR_CASE
     }
   };
+  // P^T operand of head block hb at k-block kk (16 bytes per lane)
+  const uint32_t p_lane = lds_addr(pbuf) + 16 * lane;
+  auto pp_issue = [&](int kk, int hb, bf16x8& v) {
+    switch (1024 * (2 * hb + kk)) {
+#define SLI_PP_CASE(OFF)                                                             \
+  case OFF:                                                                          \
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p_lane), "i"(OFF)); \
+    break;
+      SLI_PP_CASE(0) SLI_PP_CASE(1024) SLI_PP_CASE(2048) SLI_PP_CASE(3072)
+      SLI_PP_CASE(4096) SLI_PP_CASE(5120) SLI_PP_CASE(6144) SLI_PP_CASE(7168)
+#undef SLI_PP_CASE
+    }
+  };
+  // rescale of this wave's heads to publish with the weights (sm_finish)
+  bool pub_need = false;
+  float pub_alpha = 1.f;
 
   f32x16 o[MI];
 #pragma unroll
@@ -589,8 +674,7 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
   // more than 2^8, so weights stay below 256 (harmless in fp32 sums and bf16
   // operands) and most tiles skip the rescale.
   struct Sm {
-    f32x16 x;        // scaled logits
-    float mt;        // tile maximum (both lane halves)
+    float mt;        // tile maximum, scaled (both lane halves)
     float m_new, alpha, rs;
     bool need;       // the reference moves (wave-uniform)
     bf16x8 p[2];     // weights, the next output product's B operands
@@ -601,18 +685,16 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     return is_max ? fmaxf(a, b) : a + b;
   };
+  // The logits stay unscaled in sv: the scale (> 0) is applied to the
+  // maximum and folded into the exponentials' argument.
   auto sm_stage = [&](int st, const f32x16& sv) {
     if (st == 0) {
-#pragma unroll
-      for (int v = 0; v < 8; ++v) sm.x[v] = sv[v] * sl2;
+      sm.mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     } else if (st == 1) {
-#pragma unroll
-      for (int v = 8; v < 16; ++v) sm.x[v] = sv[v] * sl2;
+      const float m = fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15])));
+      sm.mt = fmaxf(sm.mt, m);
     } else if (st == 2) {
-      float m = fmaxf(fmaxf(sm.x[0], sm.x[1]), fmaxf(sm.x[2], sm.x[3]));
-#pragma unroll
-      for (int v = 4; v < 16; v += 2) m = fmaxf(m, fmaxf(sm.x[v], sm.x[v + 1]));
-      sm.mt = m;
+      sm.mt *= sl2;
     } else if (st == 3) {
       sm.mt = halves(sm.mt, true);
       sm.need = __ballot(sm.mt > m_run + 8.f) != 0;
@@ -621,8 +703,8 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
       sm.rs = 0.f;
     } else if (st >= 4 && st < 12) {
       const int v = 2 * (st - 4);
-      const float p0 = __builtin_amdgcn_exp2f(sm.x[v] - sm.m_new);
-      const float p1 = __builtin_amdgcn_exp2f(sm.x[v + 1] - sm.m_new);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], sl2, -sm.m_new));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v + 1], sl2, -sm.m_new));
       sm.rs += p0 + p1;
       sm.p[v >> 3][v & 7] = (__bf16)p0;
       sm.p[v >> 3][(v & 7) + 1] = (__bf16)p1;
@@ -643,17 +725,13 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
       }
       sm.rs = rs;
     }
+    // The accumulators of this wave's heads are held by every wave: the
+    // rescale factor is published with the weights and applied by each wave
+    // before the tile's output product (not at all while nothing has been
+    // accumulated).
+    pub_need = sm.need && __ballot(m_run > -1e29f) != 0;
+    pub_alpha = sm.alpha;
     if (sm.need) {
-      if (__ballot(m_run > -1e29f) != 0) {  // accumulators hold something
-        // (the accumulators stay in the accumulation registers around the
-        // scaling; without the pins the allocator moves them and spills q)
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          asm volatile("" : "+a"(o[i]));
-          o[i] *= sm.alpha;
-          asm volatile("" : "+a"(o[i]));
-        }
-      }
       l_run *= sm.alpha;
       m_run = sm.m_new;
     }
@@ -662,11 +740,45 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
     pb[1] = sm.p[1];
   };
 
+  // Writes the weights and rescale factors of `tile` (finished in registers
+  // by sm_finish) where every wave reads them; the caller waits for the
+  // writes and a barrier makes them visible.
+  auto publish = [&](int tile) {
+    const uint32_t pa = lds_addr(pbuf) + 2048 * wid + 16 * lane;
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" : : "v"(pa), "v"(pb[0]), "v"(pb[1]) : "memory");
+    const uint32_t ra = lds_addr(ring(tile)) + kRope;
+    if (pub_need && half == 0)
+      asm volatile("ds_write_b32 %0, %1" : : "v"(ra + 4 * (32 * wid + n)), "v"(pub_alpha) : "memory");
+    if (lane == 0) asm volatile("ds_write_b32 %0, %1 offset:512" : : "v"(ra + 4 * wid), "v"(pub_need ? 1 : 0) : "memory");
+  };
+  // Rescales the accumulators of the head blocks whose reference moved with
+  // `tile` (after the barrier that follows publish).
+  auto apply_rescale = [&](int tile) {
+    const uint32_t ra = lds_addr(ring(tile)) + kRope;
+    i32x4 fl;
+    asm volatile("ds_read_b128 %0, %1 offset:512\n\ts_waitcnt lgkmcnt(0)" : "=v"(fl) : "v"(ra) : "memory");
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      if (__builtin_amdgcn_readfirstlane(fl[hb]) != 0) {
+        float al;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(al) : "v"(ra + 4 * (32 * hb + n)) : "memory");
+        // (the accumulators stay in the accumulation registers around the
+        // scaling; without the pins the allocator moves them and spills q)
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          asm volatile("" : "+a"(o[4 * mm + hb]));
+          o[4 * mm + hb] *= al;
+          asm volatile("" : "+a"(o[4 * mm + hb]));
+        }
+      }
+    }
+  };
+
   // logits S^T[pos, head] of one tile (one accumulator chain: a second one
   // would not fit beside q and the output accumulators).  The operand reads
   // are instructions of their own, like the transposed reads below.
   auto av_issue = [&](uint32_t c, int k, bf16x8& v) {
-    const uint32_t p = c + abase[k & 3];
+    const uint32_t p = (c + abase) ^ (32 * (k & 3));
     switch (4096 * (k >> 2)) {
 #define SLI_AV_CASE(OFF)                                                            \
   case OFF:                                                                         \
@@ -677,10 +789,7 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
 #undef SLI_AV_CASE
     }
   };
-  // The next tile's loads are spread over the chain (one every KS / DPW
-  // steps), so a load whose issue stalls on a full memory queue does so
-  // while MFMAs are in flight.
-  auto logits = [&](const char* C, int ld_tile, const int (&pr)[4]) -> f32x16 {
+  auto logits = [&](const char* C) -> f32x16 {
     const uint32_t c = lds_addr(C);
     bf16x8 av[KS];
     f32x16 s0 = (f32x16){};
@@ -688,9 +797,6 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
     for (int k = 0; k < PDL; ++k) av_issue(c, k, av[k]);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-#ifdef SLI_LOADS_IN_LOGITS
-      if (k % (KS / DPW) == 0 && ld_tile < tiles) load_one(ld_tile, pr, k / (KS / DPW));
-#endif
       if (k + PDL < KS) av_issue(c, k + PDL, av[k + PDL]);
       switch (min(PDL, KS - 1 - k)) {
 #define SLI_AV_WAIT(N)                                                              \
@@ -705,47 +811,49 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
     }
     return s0;
   };
-  // output product O^T[d, head] += C^T[d, pos] . P^T[pos, head] of the
-  // previous tile (do_pv), with the current tile's softmax stages (do_sm)
-  // interleaved between its MFMAs
+  // Output product O^T[d, head] += C^T[d, pos] . P^T[pos, head] of the
+  // previous tile (do_pv) for this wave's 128 columns and every head, with the
+  // current tile's softmax stages (do_sm) interleaved between its MFMAs.  MFMA
+  // j: k-block kk = j / 16, column tile mm = (j / 4) % 4, head block
+  // hb = j % 4; the read schedule and its waits are described at
+  // sfa_pv_wait.
   auto outprod = [&](const char* C, bool do_pv, const f32x16& sv, bool do_sm, int ld_tile, const int (&pr)[4]) {
-    const uint32_t c = lds_addr(C);
-    int kld = 0;
-    bf16x4 lo[PVS], hi[PVS];
+    const uint32_t c = lds_addr(C) + 8192 * wid;
+    const int ld_row = tile_row(ld_tile, pr);
+    const bool do_ld = ld_tile < tiles;
+    char* const ld_dst = ring(ld_tile) + 1024 * wid_s;
+    bf16x4 lo[8], hi[8];
+    bf16x8 pv[2][4];
     if (do_pv) {
 #pragma unroll
-      for (int j = 0; j < PD; ++j) pv_issue(c, j, lo[j], hi[j]);
-    }
+      for (int hb = 0; hb < 4; ++hb) pp_issue(0, hb, pv[0][hb]);
 #pragma unroll
-    for (int j = 0; j < PVS; ++j) {
-      if (do_pv) {
-        if (j + PD < PVS) pv_issue(c, j + PD, lo[j + PD], hi[j + PD]);
-        // reads issued after step j's pair: 2 per later step in flight
-        switch (2 * min(PD, PVS - 1 - j)) {
-#define SLI_TR_WAIT(N)                                                                     \
-  case N:                                                                                  \
-    asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(lo[j]), "+v"(hi[j]));                   \
-    break;
-          SLI_TR_WAIT(0) SLI_TR_WAIT(2) SLI_TR_WAIT(4) SLI_TR_WAIT(6) SLI_TR_WAIT(8)
-#undef SLI_TR_WAIT
-        }
-        const bf16x8 cv = (bf16x8){lo[j][0], lo[j][1], lo[j][2], lo[j][3], hi[j][0], hi[j][1], hi[j][2], hi[j][3]};
-        o[j % MI] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv, pb[j / MI], o[j % MI], 0, 0, 0);
-        SLI_PIN_A(o[j % MI]);
-      }
-      if (do_sm && j % 2 == 1 && j / 2 < SM_STAGES) sm_stage(j / 2, sv);
-#ifndef SLI_LOADS_IN_LOGITS
-      // The next tile's loads go between these independent MFMAs, and the
-      // waves take turns (wave w from step (PVS / NW) w on): the CU accepts
-      // one direct-to-LDS load every ~15 cycles, so loads issued by all waves
-      // at once would keep each of them waiting for the others'.
-      if (ld_tile < tiles && ((j - (PVS / NW) * wid) & (PVS - 1)) < DPW) {
-        load_one(ld_tile, pr, kld);  // (kld counts this wave's loads of the tile)
-        ++kld;
-      }
-#endif
-      __builtin_amdgcn_sched_barrier(0);
+      for (int pi = 0; pi < kPvAhead; ++pi) pv_issue(c, 0, pi, lo[pi], hi[pi]);
     }
+    static_for<PVS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int kk = j >> 4, mm = (j >> 2) & 3, hb = j & 3, pi = 4 * kk + mm;
+      if (do_pv) {
+        if constexpr (hb == 0 && pi + kPvAhead < 8)
+          pv_issue(c, (pi + kPvAhead) >> 2, (pi + kPvAhead) & 3, lo[pi + kPvAhead], hi[pi + kPvAhead]);
+        constexpr int w = sfa_pv_outstanding(kPvAhead, j);
+        asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo[pi]), "+v"(hi[pi]), "+v"(pv[kk][hb]) : "i"(w));
+        const bf16x8 cv = (bf16x8){lo[pi][0], lo[pi][1], lo[pi][2], lo[pi][3], hi[pi][0], hi[pi][1], hi[pi][2], hi[pi][3]};
+        o[4 * mm + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv, pv[kk][hb], o[4 * mm + hb], 0, 0, 0);
+        SLI_PIN_A(o[4 * mm + hb]);
+        if constexpr (kk == 0 && mm == 3) pp_issue(1, hb, pv[1][hb]);
+      }
+      if constexpr (j % 2 == 1 && j / 2 < SM_STAGES) {
+        if (do_sm) sm_stage(j / 2, sv);
+      }
+      // The next tile's loads go between these independent MFMAs, one every
+      // third step (four waves then issue one about every 25 cycles, within
+      // the ~15 cycles per direct-to-LDS load the CU accepts).
+      if constexpr (j % 3 == 1 && j / 3 < DPW) {
+        if (do_ld) load_one(ld_dst, ld_row, j / 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // ---------------------------------------------------------------- main loop
@@ -771,8 +879,16 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
+    // every wave is past tile - 2's output product (the weights buffer is
+    // free) and tile - 1's logits (its rope columns are free)
+    if (prev) {
+      publish(tile - 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      apply_rescale(tile - 1);
+    }
     const int pr[4] = {pr_next[0], pr_next[1], pr_next[2], pr_next[3]};
-    const f32x16 sv = logits(ring(tile), tile + 2, pr);
+    const f32x16 sv = logits(ring(tile));
     if (tile + 3 < tiles) tile_rows(tile + 3, pr_next);
     const uint32_t vm_next = tile + 1 < tiles ? (uint32_t)__ballot(rows[(tile + 1) * kTileRows + n] >= 0) : 0u;
     outprod(ring(tile - 1), prev, sv, true, tile + 2, pr);
@@ -782,29 +898,45 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
   if (tiles > 0) step(0, false);
 #pragma unroll 1
   for (int tile = 1; tile < tiles; ++tile) step(tile, true);
-  if (tiles > 0) outprod(ring(tiles - 1), true, (f32x16){}, false, tiles, pr_next);
+  if (tiles > 0) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    publish(tiles - 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    apply_rescale(tiles - 1);
+    outprod(ring(tiles - 1), true, (f32x16){}, false, tiles, pr_next);
+  }
 
   // ---------------------------------------------------------------- write out
-  // The wave's O^T tile (32 heads x 512) is staged in LDS (its own ring slot,
-  // rows padded to 1040 bytes) so that each global store writes one whole
-  // 1 KiB head row.
+  // 1 / sum of every head reaches every wave through the weights buffer; the
+  // output (every head, this wave's 128 columns) is staged in LDS, head block
+  // hb in slot hb (rows padded to 1040 bytes), so that each global store
+  // writes one whole 1 KiB head row.
   SLI_WAIT_VMCNT(0);  // (prologue loads past the last tile included)
   __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();  // every wave is done with the last tile
+  __builtin_amdgcn_s_barrier();  // every wave is done with the last tile and the weights
+  float* const s_inv = reinterpret_cast<float*>(pbuf);
+  if (half == 0) s_inv[32 * wid + n] = l_run > 0.f ? 1.f / l_run : 0.f;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
   constexpr int kStageRow = 1040;
-  char* stage = ring(wid);
   {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float inv[NW];
 #pragma unroll
-    for (int m = 0; m < MI; ++m)
+    for (int hb = 0; hb < NW; ++hb) inv[hb] = s_inv[32 * hb + n];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * m + 8 * q4 + 4 * half;
-        bf16x4 v4;
+    for (int hb = 0; hb < NW; ++hb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[m][4 * q4 + i] * inv);
-        *reinterpret_cast<bf16x4*>(stage + n * kStageRow + 2 * d) = v4;
-      }
+      for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * (4 * wid + mm) + 8 * q4 + 4 * half;
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[4 * mm + hb][4 * q4 + i] * inv[hb]);
+          *reinterpret_cast<bf16x4*>(ring(hb) + n * kStageRow + 2 * d) = v4;
+        }
   }
   const size_t th = (size_t)t * a.H + head;
   const size_t ps = ((size_t)t * a.n_splits + split) * a.H + head;
@@ -817,6 +949,8 @@ __global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();  // head block wid's rows were staged by every wave
+  const char* stage = ring(wid);
   const int rows_out = min(32, a.H - 32 * wid);
   __bf16* obase = a.n_splits == 1 ? static_cast<__bf16*>(a.out) + ((size_t)t * a.H + 32 * wid) * 512
                                   : a.part_o + (((size_t)t * a.n_splits + split) * a.H + 32 * wid) * 512;
