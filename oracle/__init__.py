@@ -21,7 +21,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
-FMT = {"bf16": 0, "fp8": 1}
+FMT = {"bf16": 0, "fp8": 1, "mxfp8": 2}
 
 
 def build() -> str:
@@ -108,12 +108,15 @@ def quant_fp8_rows(x, block: int):
 
 
 def index_scores(q, w, k, vis: int, q_fmt="bf16", q_scales=None, k_fmt="bf16", k_scales=None) -> np.ndarray:
-    """fp32 scores [vis] of one token; q [64,128], w [64], k [>=vis,128]."""
+    """fp32 scores [vis] of one token; q [64,128], w [64], k [>=vis,128].
+    k_fmt "fp8": k_scales [>=vis] f32 per row; "mxfp8": k_scales [>=vis,4] E8M0."""
     q = _c(q, np.uint16 if q_fmt == "bf16" else np.uint8)
     k = _c(k, np.uint16 if k_fmt == "bf16" else np.uint8)
     w = _c(w, np.float32)
     qs = _c(q_scales, np.uint8)
-    ks = _c(k_scales, np.float32)
+    ks = _c(k_scales, np.uint8 if k_fmt == "mxfp8" else np.float32)
+    if k_fmt == "mxfp8":
+        assert ks.shape[0] >= vis and ks.shape[1] == 4
     assert q.shape == (64, 128) and w.shape == (64,) and k.shape[1] == 128 and k.shape[0] >= vis
     out = np.empty((vis,), dtype=np.float32)
     lib().oracle_index_scores(FMT[q_fmt], _p(q), _p(qs), _p(w), FMT[k_fmt], _p(k), _p(ks), vis, _p(out))
@@ -162,7 +165,8 @@ def run_tokens(case, tokens, with_attn=True):
             q, qs = case.idx_q(t, 1)
             w = case.w(t, 1)
             vis = case.visible(t)
-            sc = index_scores(q[0], w[0], k, vis, q_fmt=case.idx_fmt, q_scales=None if qs is None else qs[0],
+            q_fmt = "bf16" if case.idx_fmt == "bf16" else "fp8"  # the query is MXFP8 in both FP8 layouts
+            sc = index_scores(q[0], w[0], k, vis, q_fmt=q_fmt, q_scales=None if qs is None else qs[0],
                               k_fmt=case.idx_fmt, k_scales=ks)
             idx, n = topk(sc, case.top_k)
             r = {"scores": sc, "idx": idx, "n": n}

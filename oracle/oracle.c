@@ -34,7 +34,9 @@
  * The pages' quantised layouts ("Optimizing Inference ...", sec. 4 table):
  * indexer q in MXFP8 with one E8M0 scale per 32 elements; FP8 caches carry f32
  * scales per 128-element block (indexer key: one per row; latent: one per row,
- * or one per 128-wide tile of the row, the fifth tile being 64 wide).
+ * or one per 128-wide tile of the row, the fifth tile being 64 wide).  The
+ * indexer key may also be MXFP8 like the query (E4M3 codes, one E8M0 scale
+ * per 32 elements), the group-32 form that table gives for it.
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,7 +64,7 @@ double oracle_e8m0(uint8_t e) {
   return ldexp(1.0, (int)e - 127);
 }
 
-/* fmt 0 = bf16 bits, fmt 1 = E4M3 codes */
+/* fmt 0 = bf16 bits, fmt 1 and 2 = E4M3 codes */
 static double elem(int fmt, const void* p, int64_t i) {
   return fmt == 0 ? oracle_bf16(((const uint16_t*)p)[i]) : oracle_e4m3(((const uint8_t*)p)[i]);
 }
@@ -72,12 +74,15 @@ static double elem(int fmt, const void* p, int64_t i) {
  *   q        [64][128] bf16 bits (q_fmt 0) or E4M3 codes (q_fmt 1)
  *   q_scales [64][4] E8M0, one per 32 consecutive d (q_fmt 1 only)
  *   w        [64] f32 head weights
- *   k        [vis][128] logical key rows, bf16 (k_fmt 0) or E4M3 (k_fmt 1)
- *   k_scales [vis] f32, one per 128-element block = one per row (k_fmt 1)
+ *   k        [vis][128] logical key rows, bf16 (k_fmt 0) or E4M3 (k_fmt 1, 2)
+ *   k_scales k_fmt 1: [vis] f32, one per 128-element block = one per row;
+ *            k_fmt 2: [vis][4] E8M0, one per 32 consecutive d (MXFP8, the
+ *            indexer-key layout of the "Optimizing Inference ..." sec. 4
+ *            table: the same group-32 power-of-two scaling as the query)
  *   out      [vis] f32
  */
 void oracle_index_scores(int q_fmt, const void* q, const uint8_t* q_scales, const float* w, int k_fmt,
-                         const void* k, const float* k_scales, int64_t vis, float* out) {
+                         const void* k, const void* k_scales, int64_t vis, float* out) {
   double qd[64][128];
   for (int h = 0; h < 64; ++h)
     for (int d = 0; d < 128; ++d) {
@@ -90,7 +95,8 @@ void oracle_index_scores(int q_fmt, const void* q, const uint8_t* q_scales, cons
     double kd[128];
     for (int d = 0; d < 128; ++d) {
       double v = elem(k_fmt, k, s * 128 + d);
-      if (k_fmt == 1) v *= (double)k_scales[s];
+      if (k_fmt == 1) v *= (double)((const float*)k_scales)[s];
+      if (k_fmt == 2) v *= oracle_e8m0(((const uint8_t*)k_scales)[s * 4 + d / 32]);
       kd[d] = v;
     }
     double acc = 0.0;

@@ -25,6 +25,7 @@ _LIB = None
 
 PAGE = 64
 D_IDX = 128
+KFMT = {"bf16": 0, "fp8": 1, "mxfp8": 2}  # indexer key row formats of synth_idxk_rows
 H_IDX = 64
 D_LAT = 576
 D_V = 512
@@ -80,8 +81,10 @@ class Case:
     positions, its n_q new tokens being the last n_q of them.  Token t = b*n_q+j
     sits at absolute position seq_lens[b] - n_q + j and sees positions <= that.
 
-    idx_fmt / kv_fmt: "bf16" or "fp8".  kv_groups: FP8 latent scales per row
-    (1 = per token, 5 = tiles of 128).
+    idx_fmt: "bf16", "fp8" (MXFP8 query, key rows with one f32 scale each) or
+    "mxfp8" (MXFP8 query and key rows, one E8M0 scale per 32 elements of both).
+    kv_fmt: "bf16" or "fp8".  kv_groups: FP8 latent scales per row (1 = per
+    token, 5 = tiles of 128).
     """
     seed: int
     B: int
@@ -174,8 +177,8 @@ class Case:
         return out
 
     def k_rows(self, b: int, s0: int = 0, s1: int | None = None):
-        """Logical key rows of request b: bf16 (uint16 [n,128], None) or
-        fp8 (uint8 [n,128], f32 [n])."""
+        """Logical key rows of request b: bf16 (uint16 [n,128], None), fp8
+        (uint8 [n,128], f32 [n]) or mxfp8 (uint8 [n,128], uint8 E8M0 [n,4])."""
         s1 = int(self.seq_lens[b]) if s1 is None else s1
         n = s1 - s0
         if self.idx_fmt == "bf16":
@@ -183,13 +186,13 @@ class Case:
             lib().synth_idxk_rows(self.seed, 0, b, s0, n, _p(out), None)
             return out, None
         out = np.empty((n, D_IDX), dtype=np.uint8)
-        sc = np.empty((n,), dtype=np.float32)
-        lib().synth_idxk_rows(self.seed, 1, b, s0, n, _p(out), _p(sc))
+        sc = np.empty((n,), dtype=np.float32) if self.idx_fmt == "fp8" else np.empty((n, 4), dtype=np.uint8)
+        lib().synth_idxk_rows(self.seed, KFMT[self.idx_fmt], b, s0, n, _p(out), _p(sc))
         return out, sc
 
     def k_pool(self):
-        """Paged key pool: bf16 uint16 [NP,64,128] (scales None) or fp8 uint8
-        [NP,64,128] + f32 [NP,64]."""
+        """Paged key pool: bf16 uint16 [NP,64,128] (scales None), fp8 uint8
+        [NP,64,128] + f32 [NP,64], or mxfp8 uint8 [NP,64,128] + E8M0 [NP,64,4]."""
         NP = self.num_pages
         bt = np.ascontiguousarray(self.block_table())
         if self.idx_fmt == "bf16":
@@ -197,8 +200,9 @@ class Case:
             sc = None
         else:
             pool = np.zeros((NP, PAGE, D_IDX), dtype=np.uint8)
-            sc = np.zeros((NP, PAGE), dtype=np.float32)
-        lib().synth_fill_idxk_pool(self.seed, 0 if self.idx_fmt == "bf16" else 1, self.B, _p(self.seq_lens),
+            sc = np.zeros((NP, PAGE), dtype=np.float32) if self.idx_fmt == "fp8" else \
+                np.full((NP, PAGE, 4), 127, dtype=np.uint8)
+        lib().synth_fill_idxk_pool(self.seed, KFMT[self.idx_fmt], self.B, _p(self.seq_lens),
                                    self.max_pages, _p(bt), _p(pool), _p(sc))
         return pool, sc
 

@@ -156,7 +156,9 @@ void synth_kscale(uint64_t seed, int64_t b, int64_t s0, int64_t ns, float* out) 
 }
 
 /* fmt 0: bf16 rows [ns][128].  fmt 1: E4M3 codes [ns][128] of the integers and
- * a per-row (= per 128-element block) f32 scale in {1/2, 1}. */
+ * a per-row (= per 128-element block) f32 scale in {1/2, 1}.  fmt 2: the same
+ * codes with four E8M0 scale codes per row (one per 32 elements), each 126 or
+ * 127 (1/2 or 1), stored as 4 bytes per row where fmt 1 stores the f32. */
 void synth_idxk_rows(uint64_t seed, int fmt, int64_t b, int64_t s0, int64_t ns, void* data, float* scales) {
   e4m3_table();
   uint64_t base = stream_base(seed, ST_IDXK);
@@ -169,6 +171,9 @@ void synth_idxk_rows(uint64_t seed, int fmt, int64_t b, int64_t s0, int64_t ns, 
       else ((uint8_t*)data)[s * 128 + d] = e4m3_encode((double)v);
     }
     if (fmt == 1) scales[s] = (draw(sbase, ctr_bsd(b, s0 + s, 0, 1)) >> 63) ? 1.0f : 0.5f;
+    if (fmt == 2)
+      for (int g = 0; g < 4; ++g)
+        ((uint8_t*)scales)[s * 4 + g] = (draw(sbase, ctr_bsd(b, s0 + s, g, 4)) >> 63) ? 127 : 126;
   }
 }
 
@@ -238,6 +243,7 @@ static void fill_pool(uint64_t seed, int fmt, int G, int which, int64_t B, const
 
 void synth_fill_idxk_pool(uint64_t seed, int fmt, int64_t B, const int32_t* seq_lens, int64_t max_pages,
                           const int32_t* block_table, void* pool, float* pool_scales) {
+  /* fmt 2 stores its four scale bytes per row where fmt 1 stores one f32 */
   fill_pool(seed, fmt, 1, 0, B, seq_lens, max_pages, block_table, pool, pool_scales, fmt == 0 ? 256 : 128, 1);
 }
 

@@ -57,6 +57,21 @@ def test_generator_bounds_and_mx_exactness():
     assert (kd == c.k_int(0)).all() and set(np.unique(ks)) <= {0.5, 1.0}
 
 
+def test_generator_mxfp8_keys():
+    c = synth.Case(seed=14, B=2, n_q=1, seq_lens=[300, 130], top_k=32, H=16, idx_fmt="mxfp8")
+    k, ks = c.k_rows(1)
+    assert k.shape == (130, 128) and ks.shape == (130, 4) and ks.dtype == np.uint8
+    kd = torch.from_numpy(k).view(torch.float8_e4m3fn).double().numpy()
+    assert (kd == c.k_int(1)).all()
+    sc = torch.from_numpy(ks).view(torch.float8_e8m0fnu).double().numpy()
+    assert set(np.unique(sc)) == {0.5, 1.0}  # both values occur, independently per group
+    assert (ks[:, 0] != ks[:, 1]).any()
+    kp, kps = c.k_pool()
+    bt = c.block_table()
+    for s in range(130):
+        assert (kp[bt[1, s // 64], s % 64] == k[s]).all() and (kps[bt[1, s // 64], s % 64] == ks[s]).all()
+
+
 def test_generator_page_scatter():
     c = synth.Case(seed=12, B=3, n_q=1, seq_lens=[200, 64, 129], top_k=8, H=16, kv_fmt="fp8", kv_groups=5)
     bt = c.block_table()
@@ -73,25 +88,30 @@ def test_generator_page_scatter():
 
 
 # ---------------------------------------------------------------- indexer scores
-def _exact_scores_x64(q_int, w, k_int, k_scale=None):
-    """64 * I[s] as exact integers: w = n/32, optional per-row scale in {1/2, 1}."""
+def _exact_scores_x64(q_int, w, k_int, k_scale=None, k_group_e8m0=None):
+    """64 * I[s] as exact integers: w = n/32; optional per-row scale in {1/2, 1},
+    or per-32-element E8M0 codes in {126, 127} (scales 1/2, 1)."""
     n = np.round(w * 32).astype(np.int64)
-    dots = k_int.astype(np.int64) @ q_int.astype(np.int64).T  # [L, 64]
-    relu = np.maximum(dots, 0)
-    acc = relu @ n  # 32 * sum_h w relu(q.k)
-    mult = np.full(k_int.shape[0], 2, dtype=np.int64) if k_scale is None else np.round(2 * k_scale).astype(np.int64)
-    return acc * mult
+    k2 = 2 * k_int.astype(np.int64)  # 2 x the dequantised key, an integer
+    if k_group_e8m0 is not None:
+        k2 = k_int.astype(np.int64) * np.repeat(np.where(k_group_e8m0 == 127, 2, 1), 32, axis=1)
+    elif k_scale is not None:
+        k2 = k_int.astype(np.int64) * np.round(2 * k_scale).astype(np.int64)[:, None]
+    dots2 = k2 @ q_int.astype(np.int64).T  # [L, 64], 2 q.k
+    return np.maximum(dots2, 0) @ n  # 64 * sum_h w relu(q.k)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp8"])
 def test_scores_equal_exact_integer_arithmetic(fmt):
     c = synth.Case(seed=21, B=1, n_q=1, seq_lens=[777], top_k=64, H=16, idx_fmt=fmt)
     q, qs = c.idx_q()
     w = c.w()
     k, ks = c.k_rows(0)
-    sc = oracle.index_scores(q[0], w[0], k, 777, q_fmt=fmt, q_scales=None if qs is None else qs[0], k_fmt=fmt,
+    q_fmt = "bf16" if fmt == "bf16" else "fp8"
+    sc = oracle.index_scores(q[0], w[0], k, 777, q_fmt=q_fmt, q_scales=None if qs is None else qs[0], k_fmt=fmt,
                              k_scales=ks)
-    exact = _exact_scores_x64(c.idx_q_int()[0], w[0], c.k_int(0), ks)
+    exact = _exact_scores_x64(c.idx_q_int()[0], w[0], c.k_int(0), ks if fmt == "fp8" else None,
+                              ks if fmt == "mxfp8" else None)
     assert (sc.astype(np.float64) * 64 == exact.astype(np.float64)).all()
     assert exact.max() < 2 ** 24 * 2  # the fp32 sum is exact
 
