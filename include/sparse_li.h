@@ -36,9 +36,11 @@
  *   values (so a bad table gives wrong results, never an out-of-bounds access).
  * - Formats.  LI_BF16: bfloat16 bit patterns.  LI_FP8: OCP FP8 E4M3FN codes
  *   with block scales (positive f32 for caches, E8M0 for the indexer query).
- *   The pages' quantised layouts ("Optimizing Inference for Hybrid Attention
- *   LLMs", sec. 4 table): indexer q MXFP8 with one E8M0 scale per 32
- *   elements; FP8 caches with one f32 scale per 128-element block.
+ *   LI_MXFP8 (indexer key only): E4M3FN codes with one E8M0 scale per 32
+ *   elements, like the query.  The pages' quantised layouts ("Optimizing
+ *   Inference for Hybrid Attention LLMs", sec. 4 table): indexer q MXFP8 with
+ *   one E8M0 scale per 32 elements, the indexer key with group-32 scales too;
+ *   FP8 caches with one f32 scale per 128-element block.
  * - Return values: LI_OK, or a negative li_status; on failure nothing has been
  *   enqueued and li_last_error() describes the problem (thread-local).
  * - Results are deterministic: the same inputs give bit-identical outputs.
@@ -61,7 +63,7 @@ typedef enum {
   LI_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } li_status;
 
-typedef enum { LI_BF16 = 0, LI_FP8 = 1 } li_dtype;
+typedef enum { LI_BF16 = 0, LI_FP8 = 1, LI_MXFP8 = 2 } li_dtype;
 
 #define LI_PAGE_SIZE 64
 #define LI_INDEX_HEADS 64
@@ -96,9 +98,11 @@ li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* strea
  *   q_scales  [T,64,4]    E8M0 scales (one per 32 consecutive elements; LI_FP8 only,
  *                         must be NULL for LI_BF16)
  *   w         [T,64]      f32 per-token head weights (any sign)
- *   k_cache   [num_pages,64,128] indexer key pool; LI_BF16 bits, or LI_FP8 codes with
- *   k_scales  [num_pages,64]     one positive f32 scale per 128-element row (LI_FP8 only)
- *   k_dtype must equal q_dtype.
+ *   k_cache   [num_pages,64,128] indexer key pool; LI_BF16 bits, or E4M3 codes with
+ *   k_scales  LI_FP8:   [num_pages,64]   one positive f32 scale per 128-element row;
+ *             LI_MXFP8: [num_pages,64,4] uint8 E8M0 codes, one per 32 elements
+ *             (0..254); 4-byte aligned; NULL for LI_BF16
+ *   k_dtype   LI_BF16 with a LI_BF16 query; LI_FP8 or LI_MXFP8 with a LI_FP8 query.
  *   top_k     1..2048
  *   idx_out   [T,top_k] int32: the min(top_k, visible) positions with the largest
  *             score, ties going to the lower position, written in ascending
@@ -121,7 +125,7 @@ li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* strea
 li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                         int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q,
                         const uint8_t* q_scales, const float* w, int32_t k_dtype, const void* k_cache,
-                        const float* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
+                        const void* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /*

@@ -16,14 +16,14 @@ import os
 
 import torch
 
-__all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LiError",
+__all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LiError",
            "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
            "li_cache_append"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_li.so")
 
-LI_BF16, LI_FP8 = 0, 1
+LI_BF16, LI_FP8, LI_MXFP8 = 0, 1, 2
 LI_OK = 0
 _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKSPACE", -4: "LI_ERR_HIP"}
 
@@ -127,8 +127,9 @@ def li_score_topk(q: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, seq_l
                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Fused indexer score + Top-K.  q [T,64,128] (bf16, or uint8 E4M3 codes with
     q_scales [T,64,4] uint8 E8M0), w [T,64] f32, k_cache [NP,64,128] (bf16, or uint8
-    codes with k_scales [NP,64] f32).  Returns idx [T,top_k] int32, ascending
-    positions, -1 padded."""
+    codes with k_scales [NP,64] f32 per row, or k_scales [NP,64,4] uint8 E8M0 per
+    32 elements = MXFP8 keys).  Returns idx [T,top_k] int32, ascending positions,
+    -1 padded."""
     B = seq_lens.shape[0]
     T = q.shape[0]
     if T % B:
@@ -141,8 +142,9 @@ def li_score_topk(q: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, seq_l
     if workspace is None:
         need = li_score_topk_workspace_size(B, n_q, max_pages, top_k)
         workspace = _workspace("indexer", need, q.device)
+    k_dtype = LI_MXFP8 if k_scales is not None and k_scales.dtype == torch.uint8 else _dtype_of(k_cache)
     st = lib().li_score_topk(B, n_q, _ptr(seq_lens), _ptr(block_table), max_pages, num_pages, _dtype_of(q), _ptr(q),
-                             _ptr(q_scales), _ptr(w), _dtype_of(k_cache), _ptr(k_cache), _ptr(k_scales), top_k,
+                             _ptr(q_scales), _ptr(w), k_dtype, _ptr(k_cache), _ptr(k_scales), top_k,
                              _ptr(idx_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream))
     _check(st)

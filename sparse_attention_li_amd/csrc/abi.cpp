@@ -143,19 +143,22 @@ li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* strea
 li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                         int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q,
                         const uint8_t* q_scales, const float* w, int32_t k_dtype, const void* k_cache,
-                        const float* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
+                        const void* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
   li_status st = check_paged(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages);
   if (st != LI_OK) return st;
   if (top_k < 1 || top_k > LI_MAX_TOP_K) return fail(LI_ERR_INVALID_ARG, "top_k must be in [1, 2048] (got %d)", top_k);
   if (!q || !w || !k_cache || !idx_out) return fail(LI_ERR_INVALID_ARG, "q, w, k_cache and idx_out must not be NULL");
   if (q_dtype != LI_BF16 && q_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown q_dtype %d", q_dtype);
-  if (k_dtype != q_dtype) return fail(LI_ERR_UNSUPPORTED, "k_dtype must equal q_dtype (got %d, %d)", k_dtype, q_dtype);
   const bool fp8 = q_dtype == LI_FP8;
+  if (fp8 ? (k_dtype != LI_FP8 && k_dtype != LI_MXFP8) : k_dtype != LI_BF16)
+    return fail(LI_ERR_UNSUPPORTED, "k_dtype %d does not go with q_dtype %d (BF16 with BF16; FP8 with FP8 or MXFP8)",
+                k_dtype, q_dtype);
   if (fp8 && (!q_scales || !k_scales)) return fail(LI_ERR_INVALID_ARG, "FP8 needs q_scales and k_scales");
   if (!fp8 && (q_scales || k_scales)) return fail(LI_ERR_INVALID_ARG, "BF16 takes no scales (pass NULL)");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w))
     return fail(LI_ERR_INVALID_ARG, "q, w and k_cache must be 16-byte aligned");
+  if (fp8 && (reinterpret_cast<uintptr_t>(k_scales) & 3u)) return fail(LI_ERR_INVALID_ARG, "k_scales must be 4-byte aligned");
   if (q_per_seq > 2) {
     // prefill chunk: many causal queries per request, selection state on chip
     if (fp8) return fail(LI_ERR_UNSUPPORTED, "the prefill indexer is built for bf16 only");
@@ -201,6 +204,7 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
   a.w = w;
   a.k = k_cache;
   a.k_scales = k_scales;
+  a.k_mx = k_dtype == LI_MXFP8;
   a.idx_out = idx_out;
   char* ws = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<uint32_t*>(ws + l.off_counters);
@@ -208,6 +212,7 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
   a.cnts = reinterpret_cast<uint64_t*>(ws + l.off_cnts);
   a.cand = reinterpret_cast<uint64_t*>(ws + l.off_cand);
   a.spin_max = spin_max();
+  a.xcd_local = sli::idx_decode_xcd_local(num_seqs, l.ncm, l.chunk, device_cus()) ? 1 : 0;
   hipError_t e = sli::launch_idx_decode(a, l.chunk, fp8, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LI_OK : hip_fail(e, "indexer launch");
 }

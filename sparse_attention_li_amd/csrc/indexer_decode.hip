@@ -19,12 +19,18 @@
 //
 // Exact selection across the n chunks of a request, every workgroup writing
 // its own chunk's share of the output (kappa = the K-th largest key):
-//   1. with R = ceil(K/n), each chunk finds, from one LDS histogram of its
-//      keys, a key interval [lo_c, hi_c) holding its R-th largest key:
-//      >= R of its keys are >= lo_c and < R are >= hi_c.  Hence
-//      lo = min lo_c and hi = max hi_c bracket kappa: >= nR >= K keys are
-//      >= lo, and <= n(R-1) < K keys are >= hi.  Exchange 1 publishes the
-//      intervals;
+//   1. chunk c takes a quota R_c with K <= sum R_c < K + n and finds, from
+//      one LDS histogram of its keys, a key interval [lo_c, hi_c) holding
+//      its R_c-th largest key: >= R_c of its keys are >= lo_c and < R_c are
+//      >= hi_c.  Hence lo = min lo_c and hi = max hi_c bracket kappa:
+//      >= sum R_c >= K keys are >= lo, and <= sum (R_c - 1) < K keys are
+//      >= hi.  The quotas follow the chunks' visible positions, so every
+//      bracket sits near the same quantile and the band stays narrow: whole
+//      chunks split K evenly; when the last chunk holds only v < CHUNK of the
+//      vis visible positions it takes floor(K v / vis) (possibly 0: then its
+//      interval is empty below and ends above its largest key) and the others
+//      ceil((K - that) / (n - 1)).  Chunks past the visible ones publish an
+//      empty interval.  Exchange 1 publishes the intervals;
 //   2. keys >= hi are selected for certain; each chunk publishes its count of
 //      them and its "band" keys in [lo, hi) with their positions (exchange 2);
 //   3. every workgroup loads all band keys of the request (a few per cent of
@@ -139,7 +145,26 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
   static_assert(PER * THREADS == CHUNK && 32 % PER == 0, "chunk splits into whole bit groups per thread");
   static_assert(kMaxChunksPerSeq <= THREADS, "one thread per chunk of a request");
 
-  const int c = blockIdx.x, b = blockIdx.y;
+  // Block -> (request b, chunk c).  The hardware deals blocks to the 8 XCDs
+  // in turn (block id mod 8) and each XCD starts its blocks in id order; the
+  // chunks of a request must be resident together for the exchanges.
+  //  - spread (grids of one round): request b owns blocks b*ncm .. b*ncm+ncm-1
+  //    and chunk c runs as block b*ncm + (c + b) mod ncm, so chunk 0 of
+  //    successive requests rotates over the XCDs;
+  //  - XCD-local (grids of several rounds): request b's chunks all run on XCD
+  //    b mod 8, as blocks 8 ((b / 8) ncm + c) + b mod 8, so a request waits
+  //    only for its own XCD's earlier requests, not for the slowest XCD.
+  const uint32_t ncm_u = (uint32_t)a.n_chunks_max, bid = blockIdx.x;
+  int b, c;
+  if (a.xcd_local) {
+    const uint32_t r = bid >> 3;
+    b = (int)((r / ncm_u) * 8u + (bid & 7u));
+    c = (int)(r % ncm_u);
+  } else {
+    b = (int)(bid / ncm_u);
+    c = (int)((bid % ncm_u + ncm_u - (uint32_t)b % ncm_u) % ncm_u);
+  }
+  if (b >= a.B) return;  // padding of the XCD-local grid (departs in the caller)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 31, half = lane >> 5;
@@ -226,7 +251,9 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
       __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
     }
     if constexpr (FP8) {
-      if (lane < 32) __builtin_amdgcn_global_load_lds(a.k_scales + row0 + lane, (lds_void*)(dst + TB), 4, 0, 0);
+      if (lane < 32)
+        __builtin_amdgcn_global_load_lds(static_cast<const uint32_t*>(a.k_scales) + row0 + lane, (lds_void*)(dst + TB),
+                                         4, 0, 0);
     }
   };
   // `issued` counts this wave's vector-memory instructions; mark[s] is the
@@ -282,20 +309,27 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
         for (int mt = 0; mt < NQ * 2; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt].v[j], kb, acc[mt], 0, 0, 0);
       }
-    } else {
+    }
+    // FP8 row n's scale word: its f32 scale, or (MXFP8 keys) its four E8M0
+    // codes, group g in byte g
+    const uint32_t ksw = FP8 ? reinterpret_cast<const uint32_t*>(src + TB)[n] : 0u;
+    if constexpr (FP8) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // k-step j: row n, bytes 64 j + 16 half (chunk 4j + half) and 64 j + 32 + 16 half
         const i32x4 lo = *reinterpret_cast<const i32x4*>(src + slot(n, 4 * j + half));
         const i32x4 hi = *reinterpret_cast<const i32x4*>(src + slot(n, 4 * j + 2 + half));
         const i32x8 kb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        // this lane supplies the B scale of MX group 2j + half of row n (the
+        // same lane-half rule as the query's A scales); 127 = 1 for row scales
+        const int kbs = a.k_mx ? (int)((ksw >> (8 * (2 * j + half))) & 0xffu) : 127;
 #pragma unroll
         for (int mt = 0; mt < NQ * 2; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt].v[j], kb, acc[mt], 0, 0, 0,
-                                                                   qa[mt].scale[j], 0, 127);
+                                                                   qa[mt].scale[j], 0, kbs);
       }
     }
-    const float kscale = FP8 ? reinterpret_cast<const float*>(src + TB)[n] : 1.f;
+    const float kscale = (FP8 && !a.k_mx) ? __uint_as_float(ksw) : 1.f;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       float part = 0.f;
@@ -310,7 +344,7 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
         }
       }
       part += __shfl_xor(part, 32, kWave);
-      if constexpr (FP8) part *= kscale;  // positive per-row scale commutes with ReLU
+      if constexpr (FP8) part *= kscale;  // positive per-row scale commutes with ReLU (1 for MXFP8 keys)
       if (half == 0) {
         const int s = pos0 + n;
         const uint32_t key = (s < vis[j]) ? score_key(part) : 0u;
@@ -380,24 +414,31 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
   }
   if (!any_sel) return;  // (every workgroup of the request decides alike: no exchange)
 
-  const int R = (K + n_chunks - 1) / n_chunks;
-
-  // 1. the interval [lo_c, hi_c) holding this chunk's R-th largest key
+  // 1. the interval [lo_c, hi_c) holding this chunk's R-th largest key, R its quota
   uint32_t* hist = reinterpret_cast<uint32_t*>(lds.arena);  // [kHistBins] (the key ring is free now)
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
     if (vis[j] <= K) continue;
     const int valid = max(0, min(CHUNK, vis[j] - s0));
+    const int nv = (vis[j] + CHUNK - 1) / CHUNK;   // chunks holding visible positions (>= 1)
+    const int v_last = vis[j] - (nv - 1) * CHUNK;  // visible positions of the last of them
+    int R = (K + nv - 1) / nv;
+    if (nv > 1 && v_last < CHUNK) {
+      const int r_tail = (int)((long long)K * v_last / vis[j]);  // <= v_last (K < vis)
+      R = c == nv - 1 ? r_tail : (K - r_tail + nv - 2) / (nv - 1);
+    }
     uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       mn = min(mn, sm.mm[j][w][0]);
       mx = max(mx, sm.mm[j][w][1]);
     }
-    if (valid < R) {
-      // fewer than R keys: lo_c = 1 makes the request's lo admit every valid
-      // key (more than K of them), and fewer than R keys are >= hi_c = 1
-      if (tid == 0) sm.ref[j][0] = 1u, sm.ref[j][1] = 1u;
+    if (valid == 0) {
+      // no visible position: an empty interval, neutral for min lo and max hi
+      if (tid == 0) sm.ref[j][0] = 0xffffffffu, sm.ref[j][1] = 0u;
+    } else if (R == 0) {
+      // no quota: nothing counted at or above lo_c, and no key at or above hi_c
+      if (tid == 0) sm.ref[j][0] = 0xffffffffu, sm.ref[j][1] = min(mx, 0xfffffffeu) + 1u;
     } else if (mn == mx) {
       if (tid == 0) sm.ref[j][0] = mn, sm.ref[j][1] = mn + 1u;
     } else {
@@ -750,7 +791,7 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   // every workgroup (those without work included) departs once; the last
   // resets the count and advances the epoch for the next call
   if (threadIdx.x == 0) {
-    const uint32_t total = gridDim.x * gridDim.y;
+    const uint32_t total = gridDim.x;
     const uint32_t d = __hip_atomic_fetch_add(&grid_line[kGridDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == total - 1) {
       __hip_atomic_store(&grid_line[kGridDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -761,7 +802,8 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
 
 template <int NQ, int NW, int CHUNK, bool FP8>
 static hipError_t launch_one(const IdxDecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_chunks_max, a.B);
+  const long long blocks = a.xcd_local ? (long long)((a.B + 7) / 8) * 8 * a.n_chunks_max : (long long)a.B * a.n_chunks_max;
+  dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL((li_decode_kernel<NQ, NW, CHUNK, FP8>), grid, dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
@@ -776,6 +818,14 @@ int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus) {
   auto wgs = [&](long long ch) { return (long long)B * ((maxlen + ch - 1) / ch); };
   if ((n_q == 1 || fp8) && wgs(4096) >= cus) return 4096;
   return wgs(1024) > 2LL * cus ? 2048 : 1024;
+}
+
+// XCD-local block layout when the grid takes several rounds of the chip (one
+// workgroup per CU counted), a request's chunks fit in one XCD's CUs at once,
+// and there are enough requests (>= 2 per XCD) to balance the XCDs.
+bool idx_decode_xcd_local(int B, int n_chunks_max, int chunk, int cus) {
+  (void)chunk;
+  return B >= 16 && n_chunks_max <= cus / 8 && (long long)B * n_chunks_max > cus;
 }
 
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream) {

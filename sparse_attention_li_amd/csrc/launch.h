@@ -20,9 +20,11 @@ struct IdxDecodeArgs {
   const uint8_t* q_scales;
   const float* w;
   const void* k;
-  const float* k_scales;
+  const void* k_scales;  // 4 bytes per key row: f32 scale (FP8), or 4 E8M0 codes (k_mx)
+  bool k_mx;             // FP8 keys with one E8M0 scale per 32 elements
   int32_t* idx_out;
   int spin_max;        // polls (each ~64 cycles of sleep) before an exchange wait gives up
+  int xcd_local;       // block layout: a request's chunks on one XCD (grids of several rounds)
   // workspace
   uint32_t* counters;  // [B][kCounterStride]: arrivals, departures, give-up state, epoch
   uint64_t* refs;      // [T][n_chunks_max][2]  per chunk lo, hi (each tagged with the call's epoch)
@@ -83,6 +85,7 @@ hipError_t launch_mxfp8_quant(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_cache_append(const AppendArgs& a, hipStream_t stream);
 
 int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus);
+bool idx_decode_xcd_local(int B, int n_chunks_max, int chunk, int cus);
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);

@@ -247,16 +247,19 @@ def workload(name: str) -> Case:
     decode_b64_var_fp8   batch 64, context U[4096,131072], FP8 caches (per-token latent scale)
     prefill_4k_on_64k    4096 causal queries appended to 65536 cached, top-K 2048, bf16
     decode_b128_ctx128k_mtp2  batch 128, context 131072, 2 query tokens, FP8 caches (tile-128 latent)
+
+    and one variant: decode_b64_var_mxfp8 = decode_b64_var_fp8 with MXFP8 indexer
+    keys (one E8M0 scale per 32 elements instead of one f32 per row).
     """
     if name == "decode_b1_ctx2k":
         return Case(seed=1001, B=1, n_q=1, seq_lens=[2048], top_k=256, H=16)
     if name == "decode_b32_ctx32k":
         return Case(seed=1002, B=32, n_q=1, seq_lens=[32768] * 32, top_k=2048, H=128)
-    if name == "decode_b64_var_fp8":
+    if name in ("decode_b64_var_fp8", "decode_b64_var_mxfp8"):
         rng = np.random.default_rng(1003)
         lens = rng.integers(4096, 131072 + 1, size=64)
-        return Case(seed=1003, B=64, n_q=1, seq_lens=lens, top_k=2048, H=128, idx_fmt="fp8", kv_fmt="fp8",
-                    kv_groups=1)
+        return Case(seed=1003, B=64, n_q=1, seq_lens=lens, top_k=2048, H=128,
+                    idx_fmt="fp8" if name == "decode_b64_var_fp8" else "mxfp8", kv_fmt="fp8", kv_groups=1)
     if name == "prefill_4k_on_64k":
         return Case(seed=1004, B=1, n_q=4096, seq_lens=[65536 + 4096], top_k=2048, H=128)
     if name == "decode_b128_ctx128k_mtp2":

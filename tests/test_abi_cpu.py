@@ -43,6 +43,10 @@ def _call_topk(**over):
           k_scales=ctypes.c_void_p(0x10000)), -2),
     (dict(ws_bytes=16), -3), (dict(ws=None), -3), (dict(max_pages=10 ** 6), -2),
     (dict(q=ctypes.c_void_p(0x10004)), -1),
+    # MXFP8 keys go with an FP8 query only, need their scales, 4-byte aligned
+    (dict(k_dtype=2), -2), (dict(q_dtype=1, k_dtype=2, q_scales=ctypes.c_void_p(0x10000)), -1),
+    (dict(q_dtype=1, k_dtype=2, q_scales=ctypes.c_void_p(0x10000), k_scales=ctypes.c_void_p(0x10002)), -1),
+    (dict(q_dtype=0, k_dtype=2, k_scales=ctypes.c_void_p(0x10000)), -2),
 ])
 def test_score_topk_argument_errors(over, status):
     st, msg = _call_topk(**over)

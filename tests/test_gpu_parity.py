@@ -60,6 +60,16 @@ SMALL = {
                    kv_groups=1),
     "fp8_g5_mtp2": dict(seed=13, B=2, n_q=2, seq_lens=[3000, 700], top_k=256, H=128, idx_fmt="fp8",
                         kv_fmt="fp8", kv_groups=5),
+    # MXFP8 indexer keys (one E8M0 scale per 32 elements), 1024-position chunks and two-token calls
+    "mxk_ragged": dict(seed=22, B=3, n_q=1, seq_lens=[700, 2600, 4100], top_k=300, H=32, idx_fmt="mxfp8",
+                       kv_fmt="fp8", kv_groups=1),
+    "mxk_mtp2": dict(seed=23, B=2, n_q=2, seq_lens=[3000, 129], top_k=256, H=128, idx_fmt="mxfp8", kv_fmt="fp8",
+                     kv_groups=5),
+    # more chunks than one round of the chip: the XCD-local block layout
+    "xcd_local_ragged": dict(seed=24, B=24, n_q=1, seq_lens=[49152, 20001, 33333, 40960, 47000, 25000, 36000, 44444,
+                                                              30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,
+                                                              48000, 23000, 35000, 42000, 29000, 46000, 39000, 31000],
+                             top_k=2048, H=16),
     # prefill chunks (many causal queries per request)
     "prefill_ragged": dict(seed=19, B=1, n_q=37, seq_lens=[300], top_k=64, H=16),
     "prefill_k_gt_visible": dict(seed=20, B=2, n_q=9, seq_lens=[40, 200], top_k=128, H=32),
@@ -273,6 +283,22 @@ def test_decode_b64_var_fp8_sampled(li):
     ores = oracle.run_tokens(case, tokens)
     _check_indices(case, idx.cpu().numpy(), tokens, ores)
     _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
+
+
+def test_decode_b64_var_mxfp8_keys_sampled(li):
+    """The same 64 requests with MXFP8 indexer keys (the 4096-position chunk
+    launch of the benchmark's variant figure): indices of the sampled requests
+    against the oracle (the latent and its attention are those of the FP8
+    workload above)."""
+    case = synth.workload("decode_b64_var_mxfp8")
+    L = case.seq_lens
+    tokens = sorted({0, case.B - 1, int(np.argmin(L)), int(np.argmax(L))})
+    g = GpuCase(case, attention=False)
+    assert g.k_scales.dtype == torch.uint8 and g.k_scales.shape[-1] == 4
+    idx = g.score_topk(li)
+    torch.cuda.synchronize()
+    ores = oracle.run_tokens(case, tokens, with_attn=False)
+    _check_indices(case, idx.cpu().numpy(), tokens, ores)
 
 
 def test_decode_b128_ctx128k_mtp2_sampled(li):
