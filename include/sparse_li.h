@@ -193,9 +193,11 @@ li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint
  * position L_b - q_per_seq + j: page block_table[b][pos/64], slot pos%64.
  * Tokens whose position falls outside [0, max_pages*64) are skipped.
  *   k_new     [T,128] bf16 indexer-key rows, or NULL (no key cache update)
- *   k_dtype   LI_BF16 (copied) or LI_FP8 (codes; k_scales[page][slot] = amax/448
+ *   k_dtype   LI_BF16 (copied), LI_FP8 (codes; k_scales[page][slot] = amax/448
  *             of the row, 1 for an all-zero row; codes = fl32(x/scale) to the
- *             nearest E4M3, ties to even, saturating)
+ *             nearest E4M3, ties to even, saturating; f32 k_scales 4-byte
+ *             aligned) or LI_MXFP8 (per 32 elements, as li_quantize_mxfp8;
+ *             k_scales [num_pages,64,4] uint8 E8M0)
  *   kv_new    [T,576] bf16 latent rows (512 latent + 64 rope), or NULL
  *   kv_dtype  LI_BF16 or LI_FP8 with kv_scale_groups 1 (one scale per row) or 5
  *             (one per 128-wide tile, the fifth 64 wide); scales as for the key
@@ -204,7 +206,7 @@ li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint
  */
 li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                           int32_t max_pages, int32_t num_pages, const void* k_new, int32_t k_dtype, void* k_cache,
-                          float* k_scales, const void* kv_new, int32_t kv_dtype, void* kv_cache, float* kv_scales,
+                          void* k_scales, const void* kv_new, int32_t kv_dtype, void* kv_cache, float* kv_scales,
                           int32_t kv_scale_groups, void* stream);
 
 #ifdef __cplusplus

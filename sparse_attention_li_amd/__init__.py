@@ -204,7 +204,8 @@ def li_cache_append(seq_lens: torch.Tensor, block_table: torch.Tensor, k_new: to
                     kv_cache: torch.Tensor | None = None, k_scales: torch.Tensor | None = None,
                     kv_scales: torch.Tensor | None = None, stream=None):
     """Writes the new tokens' rows into the paged caches.  k_new [T,128] bf16 into
-    k_cache [NP,64,128] (bf16, or uint8 codes with k_scales [NP,64] f32); kv_new
+    k_cache [NP,64,128] (bf16, or uint8 codes with k_scales [NP,64] f32, or with
+    k_scales [NP,64,4] uint8 E8M0 = MXFP8 keys); kv_new
     [T,576] bf16 into kv_cache [NP,64,576] (bf16, or uint8 codes with kv_scales
     [NP,64,G] f32, G = 1 or 5).  Token t of request b goes to position
     seq_lens[b] - n_q + (t % n_q)."""
@@ -216,7 +217,9 @@ def li_cache_append(seq_lens: torch.Tensor, block_table: torch.Tensor, k_new: to
     pool = k_cache if k_cache is not None else kv_cache
     groups = 1 if kv_scales is None else (kv_scales.shape[2] if kv_scales.dim() == 3 else 1)
     st = lib().li_cache_append(B, T // B, _ptr(seq_lens), _ptr(block_table), block_table.shape[1], pool.shape[0],
-                               _ptr(k_new), LI_BF16 if k_cache is None else _dtype_of(k_cache), _ptr(k_cache),
+                               _ptr(k_new), LI_BF16 if k_cache is None else
+                               (LI_MXFP8 if k_scales is not None and k_scales.dtype == torch.uint8 else _dtype_of(k_cache)),
+                               _ptr(k_cache),
                                _ptr(k_scales), _ptr(kv_new), LI_BF16 if kv_cache is None else _dtype_of(kv_cache),
                                _ptr(kv_cache), _ptr(kv_scales), groups, _stream(stream))
     _check(st)

@@ -329,7 +329,7 @@ li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint
 
 li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                           int32_t max_pages, int32_t num_pages, const void* k_new, int32_t k_dtype, void* k_cache,
-                          float* k_scales, const void* kv_new, int32_t kv_dtype, void* kv_cache, float* kv_scales,
+                          void* k_scales, const void* kv_new, int32_t kv_dtype, void* kv_cache, float* kv_scales,
                           int32_t kv_scale_groups, void* stream) {
   li_status st = check_paged(num_seqs, q_per_seq, seq_lens, block_table, max_pages, num_pages);
   if (st != LI_OK) return st;
@@ -343,6 +343,7 @@ li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* se
   a.block_table = block_table;
   a.k_new = k_new;
   a.k_fp8 = false;
+  a.k_mx = false;
   a.k_cache = k_cache;
   a.k_scales = k_scales;
   a.kv_new = kv_new;
@@ -351,10 +352,14 @@ li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* se
   a.kv_cache = kv_cache;
   a.kv_scales = kv_scales;
   if (k_new) {
-    if (k_dtype != LI_BF16 && k_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown k_dtype %d", k_dtype);
-    a.k_fp8 = k_dtype == LI_FP8;
+    if (k_dtype != LI_BF16 && k_dtype != LI_FP8 && k_dtype != LI_MXFP8)
+      return fail(LI_ERR_UNSUPPORTED, "unknown k_dtype %d", k_dtype);
+    a.k_fp8 = k_dtype != LI_BF16;
+    a.k_mx = k_dtype == LI_MXFP8;
     if (!k_cache) return fail(LI_ERR_INVALID_ARG, "k_cache must not be NULL when k_new is given");
     if (a.k_fp8 && !k_scales) return fail(LI_ERR_INVALID_ARG, "an FP8 key cache needs k_scales");
+    if (k_dtype == LI_FP8 && (reinterpret_cast<uintptr_t>(k_scales) & 3u))
+      return fail(LI_ERR_INVALID_ARG, "f32 k_scales must be 4-byte aligned");
     if (!aligned16(k_new) || !aligned16(k_cache)) return fail(LI_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
   }
   if (kv_new) {

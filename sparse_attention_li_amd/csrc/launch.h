@@ -72,8 +72,9 @@ struct AppendArgs {
   const int32_t* block_table;
   const void* k_new;  // bf16 [T][128] or null
   bool k_fp8;
+  bool k_mx;          // FP8 key rows with E8M0 scales per 32 elements
   void* k_cache;      // [num_pages][64][128] bf16 or E4M3
-  float* k_scales;    // [num_pages][64] (FP8)
+  void* k_scales;     // [num_pages][64] f32 (FP8) or [num_pages][64][4] E8M0 (k_mx)
   const void* kv_new; // bf16 [T][576] or null
   bool kv_fp8;
   int kv_groups;      // 1 or 5 (FP8)

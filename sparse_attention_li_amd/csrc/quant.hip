@@ -12,7 +12,8 @@
 //  - the new token's indexer-key row (128) and latent row (576 = 512 + 64)
 //    written into the paged caches at its position: bf16 as is, or FP8 with
 //    an f32 scale amax / 448 per row or per 128-wide tile (the fifth tile of
-//    a latent row being 64 wide) and codes fl32(x / scale) as E4M3.
+//    a latent row being 64 wide) and codes fl32(x / scale) as E4M3, or (key
+//    rows) MXFP8 like the query.
 // Token t = b * n_q + j sits at position L_b - n_q + j of request b.
 #include "device_common.h"
 #include "launch.h"
@@ -63,17 +64,21 @@ __device__ __forceinline__ float group_max(float v, int w) {
 }
 
 // ---------------------------------------------------------------- MXFP8
+// log2 of a group's scale X = 2^(floor(log2 amax) - 8), held to E8M0's range
+// [-127, 127] (an all-zero group: X = 1; a subnormal amax: the least scale).
+__device__ __forceinline__ int mx_shift(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return e == 0 ? -127 : min(max(e - 127 - 8, -127), 127);
+}
+
 // Four lanes per 32-element group, eight elements (16 bytes) per lane.
 __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const QuantArgs a) {
   const size_t chunk = (size_t)blockIdx.x * 256 + threadIdx.x;  // 8-element chunk
   const size_t n_chunks = (size_t)a.n_rows * (a.row_len / 8);
   const bool ok = chunk < n_chunks;
   const u32x4 raw = ok ? reinterpret_cast<const u32x4*>(a.x)[chunk] : (u32x4){0u, 0u, 0u, 0u};
-  const float amax = group_max(amax8(raw), 4);
-  int sh = 0;  // log2 X, held to E8M0's range
-  if (amax > 0.f) sh = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 8;
-  if (amax > 0.f && ((__float_as_uint(amax) >> 23) & 0xffu) == 0u) sh = -127;  // (subnormal amax)
-  sh = min(max(sh, -127), 127);
+  const int sh = mx_shift(group_max(amax8(raw), 4));  // log2 X
   if (!ok) return;
   reinterpret_cast<uint2*>(a.codes)[chunk] = encode8(raw, ldexpf(1.f, -sh), 0.f);
   if ((threadIdx.x & 3) == 0) a.scales[chunk / 4] = (uint8_t)(sh + 127);
@@ -106,10 +111,16 @@ __global__ __launch_bounds__(128) void cache_append_kernel(const AppendArgs a) {
       if (lane < 16) reinterpret_cast<u32x4*>(a.k_cache)[row * 16 + lane] = raw;
       return;
     }
+    if (a.k_mx) {  // MXFP8: one E8M0 scale per 32 elements (four lanes)
+      const int sh = mx_shift(group_max(amax8(raw), 4));
+      if (lane < 16) reinterpret_cast<uint2*>(a.k_cache)[row * 16 + lane] = encode8(raw, ldexpf(1.f, -sh), 0.f);
+      if (lane < 16 && (lane & 3) == 0) static_cast<uint8_t*>(a.k_scales)[row * 4 + lane / 4] = (uint8_t)(sh + 127);
+      return;
+    }
     const float amax = group_max(amax8(raw), 16);
     const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
     if (lane < 16) reinterpret_cast<uint2*>(a.k_cache)[row * 16 + lane] = encode8(raw, 1.f, sc);
-    if (lane == 0) a.k_scales[row] = sc;
+    if (lane == 0) static_cast<float*>(a.k_scales)[row] = sc;
     return;
   }
   if (!a.kv_new) return;

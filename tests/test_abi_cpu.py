@@ -118,6 +118,7 @@ def _call_append(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(k_new=None, kv_new=None), -1), (dict(num_seqs=0), -1), (dict(seq_lens=None), -1),
     (dict(k_dtype=4), -2), (dict(k_dtype=1), -1), (dict(k_cache=None), -1), (dict(kv_dtype=1), -1),
+    (dict(k_dtype=2), -1), (dict(k_dtype=1, k_scales=ctypes.c_void_p(0x10002)), -1),
     (dict(kv_dtype=1, kv_scales=ctypes.c_void_p(0x10000), groups=3), -2), (dict(kv_cache=None), -1),
     (dict(k_new=ctypes.c_void_p(0x10008)), -1), (dict(kv_cache=ctypes.c_void_p(0x10004)), -1),
 ])

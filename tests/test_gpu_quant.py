@@ -46,16 +46,20 @@ def _pools(rng, num_pages, fp8_k, fp8_kv, groups):
     kv = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 1152), dtype=np.uint8)).cuda()
     k_pool = k[:, :, :128].contiguous() if fp8_k else k.view(torch.int16)
     kv_pool = kv[:, :, :576].contiguous() if fp8_kv else kv.view(torch.int16)
-    ks = torch.from_numpy(rng.uniform(1, 2, (num_pages, 64)).astype(np.float32)).cuda() if fp8_k else None
+    if fp8_k == "mx":
+        ks = torch.from_numpy(rng.integers(0, 255, (num_pages, 64, 4), dtype=np.uint8)).cuda()
+    else:
+        ks = torch.from_numpy(rng.uniform(1, 2, (num_pages, 64)).astype(np.float32)).cuda() if fp8_k else None
     kvs = torch.from_numpy(rng.uniform(1, 2, (num_pages, 64, groups)).astype(np.float32)).cuda() if fp8_kv else None
     return k_pool, kv_pool, ks, kvs
 
 
 @pytest.mark.parametrize("fp8_k,fp8_kv,groups,n_q", [
     (False, False, 1, 1), (True, True, 1, 1), (True, True, 5, 2), (False, True, 5, 1), (True, False, 1, 2),
+    ("mx", True, 1, 1), ("mx", False, 5, 2),   # MXFP8 key rows (E8M0 per 32 elements)
 ])
 def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
-    rng = np.random.default_rng(40 + 2 * groups + n_q + 4 * fp8_k)
+    rng = np.random.default_rng(40 + 2 * groups + n_q + 4 * (fp8_k is True) + 8 * (fp8_k == "mx"))
     B, max_pages, num_pages = 5, 6, 40
     seq_lens = np.array([1, 64, 65, 200, 384][:B], dtype=np.int32)   # (L = 1 with two new tokens: one has no slot)
     bt = np.stack([rng.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
@@ -72,7 +76,9 @@ def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
     torch.cuda.synchronize()
     # expected: the pools before, with each token's row replaced
     exp = [t.cpu().numpy().copy() if t is not None else None for t in before]
-    if fp8_k:
+    if fp8_k == "mx":
+        kc, ksc = oracle.quant_mxfp8(kb)
+    elif fp8_k:
         kc, ksc = oracle.quant_fp8_rows(kb, 128)
     if fp8_kv:
         vc, vsc = oracle.quant_fp8_rows(vb, 128 if groups == 5 else 576)
@@ -82,7 +88,10 @@ def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
         if pos < 0:
             continue
         pg, sl = bt[b, pos // 64], pos % 64
-        if fp8_k:
+        if fp8_k == "mx":
+            exp[0][pg, sl] = kc[t]
+            exp[2][pg, sl] = ksc[t]
+        elif fp8_k:
             exp[0][pg, sl] = kc[t]
             exp[2][pg, sl] = ksc[t, 0]
         else:
