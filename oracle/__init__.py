@@ -21,7 +21,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
-FMT = {"bf16": 0, "fp8": 1, "mxfp8": 2}
+FMT = {"bf16": 0, "fp8": 1, "mxfp8": 2, "fp8r": 3}
 
 
 def build() -> str:
@@ -132,7 +132,8 @@ def topk(scores, top_k: int):
 
 
 def sparse_attn(q, c, idx, sm_scale: float, c_fmt="bf16", c_scales=None, want_p=False):
-    """q [H,576] bf16 bits, c [L,576] logical latent rows, idx [K].
+    """q [H,576] bf16 bits, c [L,576] logical latent rows (c_fmt "fp8r": [L,640]
+    bytes, 512 E4M3 codes + 64 bf16 rope), idx [K].
     Returns (out [H,512] f64, lse [H] f64[, p [H,K]])."""
     q = _c(q, np.uint16)
     c = _c(c, np.uint16 if c_fmt == "bf16" else np.uint8)
@@ -140,7 +141,7 @@ def sparse_attn(q, c, idx, sm_scale: float, c_fmt="bf16", c_scales=None, want_p=
     G = 1 if cs is None else (cs.shape[1] if cs.ndim == 2 else 1)
     idx = _c(idx, np.int32)
     H, K = q.shape[0], idx.shape[0]
-    assert q.shape[1] == 576 and c.shape[1] == 576
+    assert q.shape[1] == 576 and c.shape[1] == (640 if c_fmt == "fp8r" else 576)
     assert idx.max(initial=-1) < c.shape[0]
     out = np.empty((H, 512), dtype=np.float64)
     lse = np.empty((H,), dtype=np.float64)

@@ -141,6 +141,12 @@ int64_t oracle_topk(const float* scores, int64_t vis, int64_t top_k, int32_t* id
 static double latent(int c_fmt, const void* c, const float* c_scales, int G, int64_t r, int d) {
   if (c_fmt == 0) return oracle_bf16(((const uint16_t*)c)[r * 576 + d]);
   int g = G == 1 ? 0 : d / 128;
+  if (c_fmt == 3) {
+    /* 640-byte rows: 512 E4M3 latent codes, then the 64 rope elements as bf16 */
+    const uint8_t* row = (const uint8_t*)c + r * 640;
+    if (d >= 512) return oracle_bf16((uint16_t)(row[512 + 2 * (d - 512)] | (row[513 + 2 * (d - 512)] << 8)));
+    return oracle_e4m3(row[d]) * (double)c_scales[r * G + g];
+  }
   return oracle_e4m3(((const uint8_t*)c)[r * 576 + d]) * (double)c_scales[r * G + g];
 }
 
@@ -148,7 +154,10 @@ static double latent(int c_fmt, const void* c, const float* c_scales, int G, int
  * Sparse attention of one query token.
  *   q        [H][576] bf16 bits
  *   c        [L][576] logical latent rows of the token's request, bf16 (c_fmt 0)
- *            or E4M3 codes (c_fmt 1) with f32 c_scales [L][G], G in {1, 5}
+ *            or E4M3 codes (c_fmt 1) with f32 c_scales [L][G], G in {1, 5};
+ *            or (c_fmt 3) [L][640] bytes: E4M3 codes of the 512 latent
+ *            elements with f32 c_scales [L][G], G in {1, 4} (tiles of 128),
+ *            then the 64 rope elements as bf16
  *   idx      [K] selected positions; entries < 0 are skipped
  *   out      [H][512] double,  lse [H] double (-inf when nothing is selected)
  *   p_out    optional [H][K] softmax weights (0 for skipped entries)

@@ -26,6 +26,8 @@ _LIB = None
 PAGE = 64
 D_IDX = 128
 KFMT = {"bf16": 0, "fp8": 1, "mxfp8": 2}  # indexer key row formats of synth_idxk_rows
+VFMT = {"bf16": 0, "fp8": 1, "fp8r": 2}   # latent row formats of synth_latent_rows
+LAT_ROW_BYTES = {"fp8": 576, "fp8r": 640}  # FP8 latent rows (fp8r: 512 codes + 64 bf16 rope)
 H_IDX = 64
 D_LAT = 576
 D_V = 512
@@ -83,8 +85,10 @@ class Case:
 
     idx_fmt: "bf16", "fp8" (MXFP8 query, key rows with one f32 scale each) or
     "mxfp8" (MXFP8 query and key rows, one E8M0 scale per 32 elements of both).
-    kv_fmt: "bf16" or "fp8".  kv_groups: FP8 latent scales per row (1 = per
-    token, 5 = tiles of 128).
+    kv_fmt: "bf16", "fp8" (576 E4M3 codes) or "fp8r" (512 E4M3 latent codes +
+    64 bf16 rope elements, 640 bytes).  kv_groups: FP8 latent scales per row
+    (fp8: 1 = per token, 5 = tiles of 128; fp8r: 1 or 4, over the 512 latent
+    elements only).
     """
     seed: int
     B: int
@@ -220,9 +224,9 @@ class Case:
             out = np.empty((n, D_LAT), dtype=np.uint16)
             lib().synth_latent_rows(self.seed, 0, 1, b, s0, n, _p(out), None)
             return out, None
-        out = np.empty((n, D_LAT), dtype=np.uint8)
+        out = np.empty((n, LAT_ROW_BYTES[self.kv_fmt]), dtype=np.uint8)
         sc = np.empty((n, self.kv_groups), dtype=np.float32)
-        lib().synth_latent_rows(self.seed, 1, self.kv_groups, b, s0, n, _p(out), _p(sc))
+        lib().synth_latent_rows(self.seed, VFMT[self.kv_fmt], self.kv_groups, b, s0, n, _p(out), _p(sc))
         return out, sc
 
     def latent_pool(self):
@@ -232,9 +236,9 @@ class Case:
             pool = np.zeros((NP, PAGE, D_LAT), dtype=np.uint16)
             sc = None
         else:
-            pool = np.zeros((NP, PAGE, D_LAT), dtype=np.uint8)
+            pool = np.zeros((NP, PAGE, LAT_ROW_BYTES[self.kv_fmt]), dtype=np.uint8)
             sc = np.ones((NP, PAGE, self.kv_groups), dtype=np.float32)
-        lib().synth_fill_latent_pool(self.seed, 0 if self.kv_fmt == "bf16" else 1, self.kv_groups, self.B,
+        lib().synth_fill_latent_pool(self.seed, VFMT[self.kv_fmt], self.kv_groups, self.B,
                                      _p(self.seq_lens), self.max_pages, _p(bt), _p(pool), _p(sc))
         return pool, sc
 

@@ -190,7 +190,10 @@ void synth_mlaq_bf16(uint64_t seed, int64_t H, int64_t t0, int64_t nt, uint16_t*
  * fmt 0: bf16 [ns][576] of N(0,1).
  * fmt 1: E4M3 codes [ns][576] with f32 scales [ns][G]; G = 1 (one scale per
  * row) or G = 5 (tiles of 128 along the row: 4 x 128 + 1 x 64).  Each scale is
- * amax/448 of its tile (1 for an all-zero tile), codes are nearest-even. */
+ * amax/448 of its tile (1 for an all-zero tile), codes are nearest-even.
+ * fmt 2: rows of 640 bytes, E4M3 codes of the 512 latent elements then the 64
+ * rope elements as bf16; f32 scales [ns][G] over the latent only, G = 1 (one
+ * per row) or G = 4 (tiles of 128). */
 void synth_latent_rows(uint64_t seed, int fmt, int G, int64_t b, int64_t s0, int64_t ns, void* data,
                        float* scales) {
   e4m3_table();
@@ -201,6 +204,22 @@ void synth_latent_rows(uint64_t seed, int fmt, int G, int64_t b, int64_t s0, int
     for (int d = 0; d < 576; ++d) x[d] = draw_normal(draw(base, ctr_bsd(b, s0 + s, d, 576)));
     if (fmt == 0) {
       for (int d = 0; d < 576; ++d) ((uint16_t*)data)[s * 576 + d] = f32_to_bf16_rne((float)x[d]);
+      continue;
+    }
+    if (fmt == 2) {
+      uint8_t* row = (uint8_t*)data + s * 640;
+      int tw = G == 1 ? 512 : 128;
+      for (int g = 0; g < G; ++g) {
+        double amax = 0;
+        for (int d = g * tw; d < (g + 1) * tw; ++d) amax = fabs(x[d]) > amax ? fabs(x[d]) : amax;
+        float sc = amax > 0 ? (float)(amax / 448.0) : 1.0f;
+        scales[s * G + g] = sc;
+        for (int d = g * tw; d < (g + 1) * tw; ++d) row[d] = e4m3_encode(x[d] / (double)sc);
+      }
+      for (int d = 512; d < 576; ++d) {
+        uint16_t h = f32_to_bf16_rne((float)x[d]);
+        memcpy(row + 512 + 2 * (d - 512), &h, 2);
+      }
       continue;
     }
     int tw = G == 1 ? 576 : 128;
@@ -249,5 +268,6 @@ void synth_fill_idxk_pool(uint64_t seed, int fmt, int64_t B, const int32_t* seq_
 
 void synth_fill_latent_pool(uint64_t seed, int fmt, int G, int64_t B, const int32_t* seq_lens,
                             int64_t max_pages, const int32_t* block_table, void* pool, float* pool_scales) {
-  fill_pool(seed, fmt, G, 1, B, seq_lens, max_pages, block_table, pool, pool_scales, fmt == 0 ? 1152 : 576, G);
+  fill_pool(seed, fmt, G, 1, B, seq_lens, max_pages, block_table, pool, pool_scales,
+            fmt == 0 ? 1152 : fmt == 1 ? 576 : 640, G);
 }

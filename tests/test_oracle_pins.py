@@ -223,7 +223,15 @@ def _decode_latent(c, cs):
     return d * cs.astype(np.float64)[:, tile]
 
 
-@pytest.mark.parametrize("kv", [("bf16", 1), ("fp8", 1), ("fp8", 5)])
+def _decode_latent_rope_bf16(c, cs):
+    """640-byte rows: 512 E4M3 codes scaled per row (G=1) or per 128-tile (G=4), 64 bf16 rope."""
+    lat = torch.from_numpy(np.ascontiguousarray(c[:, :512])).view(torch.float8_e4m3fn).double().numpy()
+    tile = np.arange(512) // 128 if cs.shape[1] == 4 else np.zeros(512, int)
+    rope = _bf16_to_f64(np.ascontiguousarray(c[:, 512:]).view(np.uint16))
+    return np.concatenate([lat * cs.astype(np.float64)[:, tile], rope], axis=1)
+
+
+@pytest.mark.parametrize("kv", [("bf16", 1), ("fp8", 1), ("fp8", 5), ("fp8r", 1), ("fp8r", 4)])
 def test_sparse_with_all_positions_equals_dense(kv):
     fmt, G = kv
     c = synth.Case(seed=31, B=1, n_q=1, seq_lens=[300], top_k=512, H=16, kv_fmt=fmt, kv_groups=G)
@@ -232,12 +240,30 @@ def test_sparse_with_all_positions_equals_dense(kv):
     rng = np.random.default_rng(1)
     idx = np.concatenate([rng.permutation(300), -np.ones(212, int)]).astype(np.int32)
     out, lse, p = oracle.sparse_attn(q, lat, idx, c.sm_scale, c_fmt=fmt, c_scales=lats, want_p=True)
-    cd = _bf16_to_f64(lat) if fmt == "bf16" else _decode_latent(lat, lats)
+    cd = (_bf16_to_f64(lat) if fmt == "bf16" else
+          _decode_latent(lat, lats) if fmt == "fp8" else _decode_latent_rope_bf16(lat, lats))
     ref_o, ref_lse = _dense_attention(_bf16_to_f64(q), cd, c.sm_scale)
     assert np.abs(out - ref_o).max() < 1e-12
     assert np.abs(lse - ref_lse).max() < 1e-12
     assert np.abs(p.sum(axis=1) - 1).max() < 1e-12
     assert (p[:, 300:] == 0).all()
+
+
+def test_generator_rope_bf16_latent_rows():
+    """fp8r rows: the rope is the bf16 format's rope, byte for byte; the latent
+    codes and scales are the fp8 format's over the first 512 elements (G=1:
+    one scale over the 512; G=4: per 128-tile, as fp8 with G=5 for those tiles)."""
+    kw = dict(seed=33, B=1, n_q=1, seq_lens=[130], top_k=8, H=4)
+    bf, _ = synth.Case(**kw).latent_rows(0)
+    r1, s1 = synth.Case(kv_fmt="fp8r", kv_groups=1, **kw).latent_rows(0)
+    r4, s4 = synth.Case(kv_fmt="fp8r", kv_groups=4, **kw).latent_rows(0)
+    f5, t5 = synth.Case(kv_fmt="fp8", kv_groups=5, **kw).latent_rows(0)
+    assert r1.shape == (130, 640) and s1.shape == (130, 1) and s4.shape == (130, 4)
+    for r in (r1, r4):
+        assert (np.ascontiguousarray(r[:, 512:]).view(np.uint16) == bf[:, 512:]).all()
+    assert (r4[:, :512] == f5[:, :512]).all() and (s4 == t5[:, :4]).all()
+    amax = np.abs(_bf16_to_f64(bf[:, :512])).max(axis=1)  # the generator quantises the unrounded values:
+    assert np.all(np.abs(s1[:, 0] * 448 / amax - 1) < 1e-2)  # scale = amax / 448 up to the bf16 rounding
 
 
 def test_attention_special_cases():
