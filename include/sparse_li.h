@@ -37,7 +37,8 @@
  * - Formats.  LI_BF16: bfloat16 bit patterns.  LI_FP8: OCP FP8 E4M3FN codes
  *   with block scales (positive f32 for caches, E8M0 for the indexer query).
  *   LI_MXFP8 (indexer key only): E4M3FN codes with one E8M0 scale per 32
- *   elements, like the query.  The pages' quantised layouts ("Optimizing
+ *   elements, like the query.  LI_FP8_ROPE_BF16 (latent only): FP8 latent
+ *   with the 64 rope elements kept in bf16.  The pages' quantised layouts ("Optimizing
  *   Inference for Hybrid Attention LLMs", sec. 4 table): indexer q MXFP8 with
  *   one E8M0 scale per 32 elements, the indexer key with group-32 scales too;
  *   FP8 caches with one f32 scale per 128-element block.
@@ -63,7 +64,7 @@ typedef enum {
   LI_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } li_status;
 
-typedef enum { LI_BF16 = 0, LI_FP8 = 1, LI_MXFP8 = 2 } li_dtype;
+typedef enum { LI_BF16 = 0, LI_FP8 = 1, LI_MXFP8 = 2, LI_FP8_ROPE_BF16 = 3 } li_dtype;
 
 #define LI_PAGE_SIZE 64
 #define LI_INDEX_HEADS 64
@@ -139,7 +140,10 @@ size_t sfa_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t top_k);
  *   q          [T,H,576] bf16 query (latent-absorbed 512 + rope 64), H in {16,32,64,128}
  *   kv_cache   [num_pages,64,576] latent pool; LI_BF16 bits, or LI_FP8 codes with
  *   kv_scales  [num_pages,64,G] positive f32 scales, G = kv_scale_groups:
- *              1 = one scale per row, 5 = one per 128-wide tile (the 5th is 64 wide)
+ *              1 = one scale per row, 5 = one per 128-wide tile (the 5th is 64 wide);
+ *              or LI_FP8_ROPE_BF16: [num_pages,64,640] bytes per row, the 512 latent
+ *              elements as E4M3 codes then the 64 rope elements as bf16, with
+ *              G = 1 (one scale per row) or 4 (one per 128-wide latent tile)
  *   idx        [T,top_k] int32 logical positions of the token's request; entries
  *              < 0 or >= L_b are skipped
  *   sm_scale   softmax scale applied to q.c
@@ -200,7 +204,9 @@ li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint
  *             k_scales [num_pages,64,4] uint8 E8M0)
  *   kv_new    [T,576] bf16 latent rows (512 latent + 64 rope), or NULL
  *   kv_dtype  LI_BF16 or LI_FP8 with kv_scale_groups 1 (one scale per row) or 5
- *             (one per 128-wide tile, the fifth 64 wide); scales as for the key
+ *             (one per 128-wide tile, the fifth 64 wide); scales as for the key;
+ *             or LI_FP8_ROPE_BF16 (640-byte rows, the rope copied as bf16) with
+ *             kv_scale_groups 1 or 4 over the 512 latent elements
  * Caches and scales as in li_score_topk / sfa_decode.  Asynchronous on
  * `stream`; rows of other positions are left untouched.
  */

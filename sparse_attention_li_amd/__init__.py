@@ -16,14 +16,14 @@ import os
 
 import torch
 
-__all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LiError",
+__all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LI_FP8_ROPE_BF16", "LiError",
            "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
            "li_cache_append"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_li.so")
 
-LI_BF16, LI_FP8, LI_MXFP8 = 0, 1, 2
+LI_BF16, LI_FP8, LI_MXFP8, LI_FP8_ROPE_BF16 = 0, 1, 2, 3
 LI_OK = 0
 _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKSPACE", -4: "LI_ERR_HIP"}
 
@@ -164,10 +164,13 @@ def _sfa(fn, q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None, 
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     groups = 1 if kv_scales is None else (kv_scales.shape[2] if kv_scales.dim() == 3 else 1)
+    kv_dtype = _dtype_of(kv_cache)
+    if kv_dtype == LI_FP8 and kv_cache.shape[-1] == 640:
+        kv_dtype = LI_FP8_ROPE_BF16  # 512 codes + 64 bf16 rope per row
     if workspace is None:
         workspace = _workspace("attention", sfa_workspace_size(T, H, top_k), q.device)
     st = fn(B, n_q, _ptr(seq_lens), _ptr(block_table), block_table.shape[1], kv_cache.shape[0], _ptr(q), H,
-            _dtype_of(kv_cache), _ptr(kv_cache), _ptr(kv_scales), groups, _ptr(idx), top_k, float(sm_scale), _ptr(out),
+            kv_dtype, _ptr(kv_cache), _ptr(kv_scales), groups, _ptr(idx), top_k, float(sm_scale), _ptr(out),
             _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st)
     return out, lse
@@ -175,8 +178,8 @@ def _sfa(fn, q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None, 
 
 def sfa_decode(q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None, **kw):
     """Sparse MLA attention.  q [T,H,576] bf16, kv_cache [NP,64,576] (bf16, or uint8
-    codes with kv_scales [NP,64,G] f32), idx [T,K] int32.  Returns (out [T,H,512]
-    bf16, lse [T,H] f32)."""
+    codes with kv_scales [NP,64,G] f32; or uint8 [NP,64,640] = 512 codes + 64 bf16
+    rope with G = 1 or 4), idx [T,K] int32.  Returns (out [T,H,512] bf16, lse [T,H] f32)."""
     return _sfa(lib().sfa_decode, q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales, **kw)
 
 
@@ -220,6 +223,8 @@ def li_cache_append(seq_lens: torch.Tensor, block_table: torch.Tensor, k_new: to
                                _ptr(k_new), LI_BF16 if k_cache is None else
                                (LI_MXFP8 if k_scales is not None and k_scales.dtype == torch.uint8 else _dtype_of(k_cache)),
                                _ptr(k_cache),
-                               _ptr(k_scales), _ptr(kv_new), LI_BF16 if kv_cache is None else _dtype_of(kv_cache),
+                               _ptr(k_scales), _ptr(kv_new),
+                               LI_BF16 if kv_cache is None else
+                               (LI_FP8_ROPE_BF16 if kv_cache.shape[-1] == 640 else _dtype_of(kv_cache)),
                                _ptr(kv_cache), _ptr(kv_scales), groups, _stream(stream))
     _check(st)

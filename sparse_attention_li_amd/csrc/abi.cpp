@@ -239,12 +239,15 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
   if (!q || !kv_cache || !idx || !out) return fail(LI_ERR_INVALID_ARG, "q, kv_cache, idx and out must not be NULL");
   if (num_heads != 16 && num_heads != 32 && num_heads != 64 && num_heads != 128)
     return fail(LI_ERR_UNSUPPORTED, "num_heads must be 16, 32, 64 or 128 (got %d)", num_heads);
-  if (kv_dtype != LI_BF16 && kv_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
-  const bool fp8 = kv_dtype == LI_FP8;
+  if (kv_dtype != LI_BF16 && kv_dtype != LI_FP8 && kv_dtype != LI_FP8_ROPE_BF16)
+    return fail(LI_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+  const bool fp8 = kv_dtype != LI_BF16, rope16 = kv_dtype == LI_FP8_ROPE_BF16;
   if (fp8) {
     if (!kv_scales) return fail(LI_ERR_INVALID_ARG, "FP8 latent cache needs kv_scales");
-    if (kv_scale_groups != 1 && kv_scale_groups != 5)
+    if (!rope16 && kv_scale_groups != 1 && kv_scale_groups != 5)
       return fail(LI_ERR_UNSUPPORTED, "kv_scale_groups must be 1 or 5 (got %d)", kv_scale_groups);
+    if (rope16 && kv_scale_groups != 1 && kv_scale_groups != 4)
+      return fail(LI_ERR_UNSUPPORTED, "kv_scale_groups must be 1 or 4 with a bf16 rope (got %d)", kv_scale_groups);
   } else if (kv_scales) {
     return fail(LI_ERR_INVALID_ARG, "BF16 latent cache takes no scales (pass NULL)");
   }
@@ -262,6 +265,7 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
   a.num_pages = num_pages;
   a.top_k = top_k;
   a.kv_groups = fp8 ? kv_scale_groups : 1;
+  a.rope_bf16 = rope16 ? 1 : 0;
   a.n_splits = s;
   a.split_len = len;
   a.head_blocks = (num_heads + sli::sfa_heads_per_block(num_heads, fp8) - 1) / sli::sfa_heads_per_block(num_heads, fp8);
@@ -348,6 +352,7 @@ li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* se
   a.k_scales = k_scales;
   a.kv_new = kv_new;
   a.kv_fp8 = false;
+  a.kv_rope_bf16 = false;
   a.kv_groups = 1;
   a.kv_cache = kv_cache;
   a.kv_scales = kv_scales;
@@ -363,14 +368,18 @@ li_status li_cache_append(int32_t num_seqs, int32_t q_per_seq, const int32_t* se
     if (!aligned16(k_new) || !aligned16(k_cache)) return fail(LI_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
   }
   if (kv_new) {
-    if (kv_dtype != LI_BF16 && kv_dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
-    a.kv_fp8 = kv_dtype == LI_FP8;
+    if (kv_dtype != LI_BF16 && kv_dtype != LI_FP8 && kv_dtype != LI_FP8_ROPE_BF16)
+      return fail(LI_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+    a.kv_fp8 = kv_dtype != LI_BF16;
+    a.kv_rope_bf16 = kv_dtype == LI_FP8_ROPE_BF16;
     if (!kv_cache) return fail(LI_ERR_INVALID_ARG, "kv_cache must not be NULL when kv_new is given");
     if (a.kv_fp8) {
       if (!kv_scales) return fail(LI_ERR_INVALID_ARG, "an FP8 latent cache needs kv_scales");
-      if (kv_scale_groups != 1 && kv_scale_groups != 5)
+      if (!a.kv_rope_bf16 && kv_scale_groups != 1 && kv_scale_groups != 5)
         return fail(LI_ERR_UNSUPPORTED, "kv_scale_groups must be 1 (per row) or 5 (per 128-wide tile), got %d",
                     kv_scale_groups);
+      if (a.kv_rope_bf16 && kv_scale_groups != 1 && kv_scale_groups != 4)
+        return fail(LI_ERR_UNSUPPORTED, "kv_scale_groups must be 1 or 4 with a bf16 rope, got %d", kv_scale_groups);
       a.kv_groups = kv_scale_groups;
     }
     if (!aligned16(kv_new) || !aligned16(kv_cache)) return fail(LI_ERR_INVALID_ARG, "kv_new and kv_cache must be 16-byte aligned");

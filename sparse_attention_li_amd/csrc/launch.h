@@ -45,6 +45,7 @@ struct IdxPrefillArgs {
 
 struct SfaArgs {
   int T, n_q, H, max_pages, num_pages, top_k, kv_groups;
+  int rope_bf16;  // FP8 latent rows of 640 bytes: 512 codes + 64 bf16 rope (scales over the latent only)
   int n_splits, split_len, head_blocks;
   float sm_scale;
   const int32_t* seq_lens;
@@ -77,7 +78,8 @@ struct AppendArgs {
   void* k_scales;     // [num_pages][64] f32 (FP8) or [num_pages][64][4] E8M0 (k_mx)
   const void* kv_new; // bf16 [T][576] or null
   bool kv_fp8;
-  int kv_groups;      // 1 or 5 (FP8)
+  bool kv_rope_bf16;  // FP8 latent rows of 640 bytes with the 64 rope elements in bf16
+  int kv_groups;      // 1 or 5 (FP8), 1 or 4 (kv_rope_bf16)
   void* kv_cache;     // [num_pages][64][576] bf16 or E4M3
   float* kv_scales;   // [num_pages][64][kv_groups] (FP8)
 };

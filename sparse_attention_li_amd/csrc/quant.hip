@@ -13,7 +13,8 @@
 //    written into the paged caches at its position: bf16 as is, or FP8 with
 //    an f32 scale amax / 448 per row or per 128-wide tile (the fifth tile of
 //    a latent row being 64 wide) and codes fl32(x / scale) as E4M3, or (key
-//    rows) MXFP8 like the query.
+//    rows) MXFP8 like the query, or (latent rows) FP8 latent with the rope
+//    kept in bf16 (scales per row or per 128-wide tile of the 512 latent).
 // Token t = b * n_q + j sits at position L_b - n_q + j of request b.
 #include "device_common.h"
 #include "launch.h"
@@ -130,6 +131,16 @@ __global__ __launch_bounds__(128) void cache_append_kernel(const AppendArgs a) {
   if (!a.kv_fp8) {
     reinterpret_cast<u32x4*>(a.kv_cache)[row * 72 + lane] = lat;
     if (lane < 8) reinterpret_cast<u32x4*>(a.kv_cache)[row * 72 + 64 + lane] = rope;
+    return;
+  }
+  if (a.kv_rope_bf16) {  // 640-byte rows: latent codes (scales over the latent only), then the rope as is
+    const float am = group_max(amax8(lat), a.kv_groups == 1 ? 64 : 16);
+    const float sc = am > 0.f ? __fdiv_rn(am, 448.f) : 1.f;
+    uint8_t* dst = static_cast<uint8_t*>(a.kv_cache) + row * 640;
+    reinterpret_cast<uint2*>(dst)[lane] = encode8(lat, 1.f, sc);
+    if (lane < 8) reinterpret_cast<u32x4*>(dst + 512)[lane] = rope;
+    float* scp = a.kv_scales + row * a.kv_groups;
+    if (a.kv_groups == 1 ? lane == 0 : (lane & 15) == 0) scp[lane >> 4] = sc;
     return;
   }
   float sc_lat, sc_rope;

@@ -80,7 +80,7 @@ __device__ __forceinline__ void fp8x16_to_bf16(const i32x4& raw, float scale, bf
 // the index slice [split*split_len, ...) of that token.  One wave per SIMD:
 // the 576-wide q^T operands (144 VGPRs) and the 32x512 fp32 output
 // accumulators (256 registers) stay resident for the whole slice.
-template <int NHG, int WPH, bool FP8>
+template <int NHG, int WPH, bool FP8, bool ROPE16 = false>
 __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
   constexpr int NW = NHG * WPH;     // waves
   constexpr int KS = 36 / WPH;      // 16-wide logit k-steps per wave
@@ -178,7 +178,12 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     }
   };
   // FP8: codes go through registers, are scaled to bf16 and stored swizzled.
-  constexpr int F8_CHUNKS = kTileRows * 36;  // 16-code chunks per tile
+  // A row is 36 16-byte units of codes (576 bytes), or with ROPE16 32 units
+  // of latent codes followed by 8 units of bf16 rope (640 bytes), the rope
+  // units landing unchanged in tile chunks 64..71.
+  constexpr int F8_UNITS = ROPE16 ? 40 : 36;
+  constexpr int F8_ROW = 16 * F8_UNITS;
+  constexpr int F8_CHUNKS = kTileRows * F8_UNITS;  // 16-byte units per tile
   constexpr int F8_PER = (F8_CHUNKS + NT - 1) / NT;
   i32x4 f8_stage[FP8 ? F8_PER : 1];
   auto load_f8 = [&](int tile) {
@@ -187,11 +192,11 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
       const int f = tid + r * NT;
       f8_stage[r] = (i32x4){0, 0, 0, 0};
       if (f < F8_CHUNKS) {
-        const int row = f / 36, ch = f % 36;
+        const int row = f / F8_UNITS, ch = f % F8_UNITS;
         const int pr = rows[tile * kTileRows + row];
         if (pr >= 0)
           f8_stage[r] = __builtin_nontemporal_load(
-              reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(a.kv) + (size_t)pr * 576) + ch);
+              reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(a.kv) + (size_t)pr * F8_ROW) + ch);
       }
     }
   };
@@ -200,7 +205,11 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     for (int r = 0; r < F8_PER; ++r) {
       const int f = tid + r * NT;
       if (f < F8_CHUNKS) {
-        const int row = f / 36, ch = f % 36;
+        const int row = f / F8_UNITS, ch = f % F8_UNITS;
+        if (ROPE16 && ch >= 32) {  // eight bf16 rope elements (zero for a skipped entry)
+          *reinterpret_cast<i32x4*>(dst + tile_off(row, 32 + ch)) = f8_stage[r];
+          continue;
+        }
         const int pr = rows[tile * kTileRows + row];
         const float sc =
             pr >= 0 ? a.kv_scales[(size_t)pr * a.kv_groups + (a.kv_groups == 1 ? 0 : min(ch >> 3, 4))] : 0.f;
@@ -1019,11 +1028,11 @@ static hipError_t launch_combine(const SfaArgs& a, hipStream_t stream) {
 
 // Workgroups of up to 64 heads (one or two 32-head groups): FP8 rows, and
 // bf16 rows when the token has at most 64 heads.
-template <int NHG, bool FP8>
+template <int NHG, bool FP8, bool ROPE16 = false>
 static hipError_t launch_sfa_blocks(const SfaArgs& a, hipStream_t stream) {
   const int items = a.n_splits * a.T;
   dim3 grid(((items + 7) / 8) * 8 * a.head_blocks);
-  hipLaunchKernelGGL((sfa_kernel<NHG, 2, FP8>), grid, dim3(NHG * 2 * 64), 0, stream, a);
+  hipLaunchKernelGGL((sfa_kernel<NHG, 2, FP8, ROPE16>), grid, dim3(NHG * 2 * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_combine(a, stream);
 }
@@ -1039,6 +1048,8 @@ static hipError_t launch_sfa_bf16(const SfaArgs& a, hipStream_t stream) {
 int sfa_heads_per_block(int H, bool fp8) { return (fp8 || H <= 64) ? (H <= 32 ? 32 : 64) : 128; }
 
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream) {
+  if (fp8 && a.rope_bf16)
+    return a.H <= 32 ? launch_sfa_blocks<1, true, true>(a, stream) : launch_sfa_blocks<2, true, true>(a, stream);
   if (fp8) return a.H <= 32 ? launch_sfa_blocks<1, true>(a, stream) : launch_sfa_blocks<2, true>(a, stream);
   if (a.H <= 32) return launch_sfa_blocks<1, false>(a, stream);
   if (a.H <= 64) return launch_sfa_blocks<2, false>(a, stream);

@@ -38,10 +38,11 @@ class GpuCase:
         elif attention:
             self.mla_q = _t(case.mla_q(), dev)
             NP, fp8 = case.num_pages, case.kv_fmt != "bf16"
-            self.kv_pool = torch.zeros((NP, 64, 576), dtype=torch.uint8 if fp8 else torch.int16, device=dev)
+            row = 640 if case.kv_fmt == "fp8r" else 576
+            self.kv_pool = torch.zeros((NP, 64, row), dtype=torch.uint8 if fp8 else torch.int16, device=dev)
             self.kv_scales = torch.ones((NP, 64, case.kv_groups), dtype=torch.float32, device=dev) if fp8 else None
             bt = case.block_table()
-            flat = self.kv_pool.view(NP * 64, 576)
+            flat = self.kv_pool.view(NP * 64, row)
             for b in latent_requests:
                 L = int(case.seq_lens[b])
                 rows, sc = case.latent_rows(b)

@@ -66,7 +66,8 @@ def _call_sfa(fn="sfa_decode", **over):
 
 @pytest.mark.parametrize("fn", ["sfa_decode", "sfa_prefill"])
 @pytest.mark.parametrize("over,status", [
-    (dict(H=48), -2), (dict(H=256), -2), (dict(top_k=0), -1), (dict(idx=None), -1), (dict(kv_dtype=3), -2),
+    (dict(H=48), -2), (dict(H=256), -2), (dict(top_k=0), -1), (dict(idx=None), -1), (dict(kv_dtype=7), -2),
+    (dict(kv_dtype=3), -1), (dict(kv_dtype=3, kv_scales=ctypes.c_void_p(0x10000), groups=5), -2),
     (dict(kv_dtype=1), -1), (dict(kv_dtype=1, kv_scales=ctypes.c_void_p(0x10000), groups=2), -2),
     (dict(kv_scales=ctypes.c_void_p(0x10000)), -1), (dict(sm=float("nan")), -1), (dict(ws_bytes=8), -3),
     (dict(out=ctypes.c_void_p(0x10002)), -1),

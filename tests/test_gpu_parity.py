@@ -12,7 +12,7 @@ from tests.gpu_inputs import GpuCase, rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "fp8": 5e-2}
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "fp8r": 5e-2}
 
 
 @pytest.fixture(scope="module")
@@ -65,6 +65,11 @@ SMALL = {
                        kv_fmt="fp8", kv_groups=1),
     "mxk_mtp2": dict(seed=23, B=2, n_q=2, seq_lens=[3000, 129], top_k=256, H=128, idx_fmt="mxfp8", kv_fmt="fp8",
                      kv_groups=5),
+    # FP8 latent with the rope in bf16 (640-byte rows), scales per row or per 128-wide latent tile
+    "fp8r_g1_h16": dict(seed=25, B=2, n_q=1, seq_lens=[1500, 2600], top_k=300, H=16, idx_fmt="fp8", kv_fmt="fp8r",
+                        kv_groups=1),
+    "fp8r_g4_mtp2": dict(seed=26, B=2, n_q=2, seq_lens=[3000, 700], top_k=256, H=128, idx_fmt="mxfp8",
+                         kv_fmt="fp8r", kv_groups=4),
     # more chunks than one round of the chip: the XCD-local block layout
     "xcd_local_ragged": dict(seed=24, B=24, n_q=1, seq_lens=[49152, 20001, 33333, 40960, 47000, 25000, 36000, 44444,
                                                               30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,

@@ -45,7 +45,7 @@ def _pools(rng, num_pages, fp8_k, fp8_kv, groups):
     k = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 256), dtype=np.uint8)).cuda()
     kv = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 1152), dtype=np.uint8)).cuda()
     k_pool = k[:, :, :128].contiguous() if fp8_k else k.view(torch.int16)
-    kv_pool = kv[:, :, :576].contiguous() if fp8_kv else kv.view(torch.int16)
+    kv_pool = kv[:, :, :(640 if fp8_kv == "rope16" else 576)].contiguous() if fp8_kv else kv.view(torch.int16)
     if fp8_k == "mx":
         ks = torch.from_numpy(rng.integers(0, 255, (num_pages, 64, 4), dtype=np.uint8)).cuda()
     else:
@@ -57,9 +57,10 @@ def _pools(rng, num_pages, fp8_k, fp8_kv, groups):
 @pytest.mark.parametrize("fp8_k,fp8_kv,groups,n_q", [
     (False, False, 1, 1), (True, True, 1, 1), (True, True, 5, 2), (False, True, 5, 1), (True, False, 1, 2),
     ("mx", True, 1, 1), ("mx", False, 5, 2),   # MXFP8 key rows (E8M0 per 32 elements)
+    (True, "rope16", 1, 1), ("mx", "rope16", 4, 2),  # FP8 latent with the rope in bf16 (640-byte rows)
 ])
 def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
-    rng = np.random.default_rng(40 + 2 * groups + n_q + 4 * (fp8_k is True) + 8 * (fp8_k == "mx"))
+    rng = np.random.default_rng(40 + 2 * groups + n_q + 4 * (fp8_k is True) + 8 * (fp8_k == "mx") + 16 * (fp8_kv == "rope16"))
     B, max_pages, num_pages = 5, 6, 40
     seq_lens = np.array([1, 64, 65, 200, 384][:B], dtype=np.int32)   # (L = 1 with two new tokens: one has no slot)
     bt = np.stack([rng.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
@@ -80,7 +81,10 @@ def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
         kc, ksc = oracle.quant_mxfp8(kb)
     elif fp8_k:
         kc, ksc = oracle.quant_fp8_rows(kb, 128)
-    if fp8_kv:
+    if fp8_kv == "rope16":
+        lc, vsc = oracle.quant_fp8_rows(np.ascontiguousarray(vb[:, :512]), 128 if groups == 4 else 512)
+        vc = np.concatenate([lc, np.ascontiguousarray(vb[:, 512:]).view(np.uint8)], axis=1)  # rope bytes as is
+    elif fp8_kv:
         vc, vsc = oracle.quant_fp8_rows(vb, 128 if groups == 5 else 576)
     for t in range(T):
         b, j = divmod(t, n_q)
