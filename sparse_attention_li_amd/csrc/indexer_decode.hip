@@ -836,6 +836,10 @@ hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStr
     if (a.n_q == 1) return fp8 ? launch_one<1, 4, 2048, true>(a, stream) : launch_one<1, 4, 2048, false>(a, stream);
     if (a.n_q == 2) return fp8 ? launch_one<2, 4, 2048, true>(a, stream) : launch_one<2, 4, 2048, false>(a, stream);
   } else if (chunk == 4096) {
+    // FP8 grids of several rounds: four-wave workgroups (56 / 72 KiB of LDS), two per CU, so one
+    // streams while the other selects (eight-wave ones fill a CU alone)
+    if (fp8 && a.xcd_local)
+      return a.n_q == 1 ? launch_one<1, 4, 4096, true>(a, stream) : launch_one<2, 4, 4096, true>(a, stream);
     if (a.n_q == 1) return fp8 ? launch_one<1, 8, 4096, true>(a, stream) : launch_one<1, 8, 4096, false>(a, stream);
     if (a.n_q == 2 && fp8) return launch_one<2, 8, 4096, true>(a, stream);
   }

@@ -75,6 +75,11 @@ SMALL = {
                                                               30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,
                                                               48000, 23000, 35000, 42000, 29000, 46000, 39000, 31000],
                              top_k=2048, H=16),
+    # FP8 keys over more chunks than one round: four-wave workgroups, two per CU
+    "xcd_local_fp8": dict(seed=27, B=24, n_q=1, seq_lens=[49152, 20001, 33333, 40960, 47000, 25000, 36000, 44444,
+                                                           30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,
+                                                           48000, 23000, 35000, 42000, 29000, 46000, 39000, 31000],
+                          top_k=2048, H=16, idx_fmt="mxfp8", kv_fmt="fp8"),
     # prefill chunks (many causal queries per request)
     "prefill_ragged": dict(seed=19, B=1, n_q=37, seq_lens=[300], top_k=64, H=16),
     "prefill_k_gt_visible": dict(seed=20, B=2, n_q=9, seq_lens=[40, 200], top_k=128, H=32),
@@ -203,7 +208,7 @@ def test_repeated_calls_identical_many_chunks(li):
 
 
 @pytest.mark.parametrize("spin", [0, 3])
-@pytest.mark.parametrize("name", ["ragged3", "mtp2", "k2048", "fp8_g5_mtp2"])
+@pytest.mark.parametrize("name", ["ragged3", "mtp2", "k2048", "fp8_g5_mtp2", "xcd_local_fp8"])
 def test_exchange_fallbacks_stay_exact(li, monkeypatch, name, spin):
     """The decode indexer's cross-workgroup exchanges with (almost) no patience:
     most waits time out, so workgroups publish every key, give up their share
