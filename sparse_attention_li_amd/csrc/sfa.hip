@@ -10,15 +10,18 @@
 //
 // Decomposition.  A workgroup owns one token, a block of up to 64 heads and a
 // contiguous slice of the token's index row (a "split").  Each 32-head group
-// is handled by a pair of waves, one per SIMD: for the logits each wave of the
-// pair takes half of the 576-wide contraction (and the pair adds partials
-// through LDS), for the output each takes 256 of the 512 columns, so the
-// query operands (72 VGPRs) and the fp32 output accumulators (128) stay in
-// registers for the whole slice.  Per 32-row tile:
+// is handled by WPH waves: for the logits each takes 1/WPH of the 576-wide
+// contraction (the group's waves add partials through LDS), for the output
+// 512/WPH of the columns, so its share of the query operands and of the fp32
+// output accumulators stays in registers for the whole slice.  bf16 rows use
+// two waves per group (one per SIMD, 72 + 128 registers); FP8 rows four (two
+// per SIMD, 36 + 64 registers), whose second wave on each SIMD covers the
+// dequantisation and the exposed gather latency of the first.  Per 32-row tile:
 //   - the selected rows are gathered into LDS: bf16 rows by direct
 //     global-to-LDS loads through a three-deep ring (two tiles in flight while
-//     one is consumed), FP8 rows through registers, dequantised on the way in
-//     (block scale x E4M3 code);
+//     one is consumed), FP8 rows through registers (codes and block scales
+//     of the next tile loaded while the current one is consumed), dequantised
+//     on the way in (block scale x E4M3 code);
 //   - logits are computed transposed, S^T[pos, head] = C_tile . q^T, on 32x32
 //     MFMA tiles.  In this layout a lane owns one head, so the running max,
 //     the running sum and the rescale of the output accumulators are per-lane
@@ -186,17 +189,22 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
   constexpr int F8_CHUNKS = kTileRows * F8_UNITS;  // 16-byte units per tile
   constexpr int F8_PER = (F8_CHUNKS + NT - 1) / NT;
   i32x4 f8_stage[FP8 ? F8_PER : 1];
+  float f8_sc[FP8 ? F8_PER : 1];  // block scale of each staged unit, loaded with it
   auto load_f8 = [&](int tile) {
 #pragma unroll
     for (int r = 0; r < F8_PER; ++r) {
       const int f = tid + r * NT;
       f8_stage[r] = (i32x4){0, 0, 0, 0};
+      f8_sc[r] = 0.f;
       if (f < F8_CHUNKS) {
         const int row = f / F8_UNITS, ch = f % F8_UNITS;
         const int pr = rows[tile * kTileRows + row];
-        if (pr >= 0)
+        if (pr >= 0) {
           f8_stage[r] = __builtin_nontemporal_load(
               reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(a.kv) + (size_t)pr * F8_ROW) + ch);
+          if (!(ROPE16 && ch >= 32))
+            f8_sc[r] = a.kv_scales[(size_t)pr * a.kv_groups + (a.kv_groups == 1 ? 0 : min(ch >> 3, 4))];
+        }
       }
     }
   };
@@ -210,11 +218,8 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
           *reinterpret_cast<i32x4*>(dst + tile_off(row, 32 + ch)) = f8_stage[r];
           continue;
         }
-        const int pr = rows[tile * kTileRows + row];
-        const float sc =
-            pr >= 0 ? a.kv_scales[(size_t)pr * a.kv_groups + (a.kv_groups == 1 ? 0 : min(ch >> 3, 4))] : 0.f;
         bf16x8 lo8, hi8;
-        fp8x16_to_bf16(f8_stage[r], sc, lo8, hi8);
+        fp8x16_to_bf16(f8_stage[r], f8_sc[r], lo8, hi8);
         *reinterpret_cast<bf16x8*>(dst + tile_off(row, 2 * ch)) = lo8;
         *reinterpret_cast<bf16x8*>(dst + tile_off(row, 2 * ch + 1)) = hi8;
       }
@@ -264,8 +269,8 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) av[k] = *reinterpret_cast<const bf16x8*>(T + tile_off(n, 2 * (KS * part + k) + half));
     // bf16: two independent accumulator chains (even and odd k-steps) halve
-    // the dependent MFMA latency of the logits; the FP8 variant keeps one
-    // chain (its staging registers leave no room for the second)
+    // the dependent MFMA latency of the logits; the FP8 variant (four waves
+    // per group, nine k-steps each) measured no faster with two and keeps one
     f32x16 s = (f32x16){};
     if constexpr (!FP8) {
       f32x16 s_odd = (f32x16){};
@@ -305,9 +310,7 @@ __global__ __launch_bounds__(NHG * WPH * 64) void sfa_kernel(const SfaArgs a) {
     // maximum exceeds it by more than 2^8; otherwise the weights exp2(x -
     // m_run) stay below 256, harmless in fp32 sums and bf16 operands.  The
     // decision is wave-uniform, so most tiles skip the rescale entirely.
-    // (The FP8 single-head-group variant keeps the branch-free update: its
-    // staging registers leave no room for the branch.)
-    if (FP8 && NHG == 1 ? true : __ballot(mt > m_run + 8.f) != 0) {
+    if (__ballot(mt > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = exp2f(m_run - m_new);
       l_run *= alpha;
@@ -1026,13 +1029,14 @@ static hipError_t launch_combine(const SfaArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Workgroups of up to 64 heads (one or two 32-head groups): FP8 rows, and
-// bf16 rows when the token has at most 64 heads.
+// Workgroups of up to 64 heads (one or two 32-head groups): FP8 rows (four
+// waves per group), and bf16 rows when the token has at most 64 heads (two).
 template <int NHG, bool FP8, bool ROPE16 = false>
 static hipError_t launch_sfa_blocks(const SfaArgs& a, hipStream_t stream) {
   const int items = a.n_splits * a.T;
   dim3 grid(((items + 7) / 8) * 8 * a.head_blocks);
-  hipLaunchKernelGGL((sfa_kernel<NHG, 2, FP8, ROPE16>), grid, dim3(NHG * 2 * 64), 0, stream, a);
+  constexpr int WPH = FP8 ? 4 : 2;
+  hipLaunchKernelGGL((sfa_kernel<NHG, WPH, FP8, ROPE16>), grid, dim3(NHG * WPH * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_combine(a, stream);
 }
