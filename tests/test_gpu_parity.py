@@ -70,6 +70,11 @@ SMALL = {
                         kv_groups=1),
     "fp8r_g4_mtp2": dict(seed=26, B=2, n_q=2, seq_lens=[3000, 700], top_k=256, H=128, idx_fmt="mxfp8",
                          kv_fmt="fp8r", kv_groups=4),
+    # FP8 latent with 64 heads: one workgroup per token slice, both 32-head groups in it
+    "fp8_h64_ragged": dict(seed=27, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=520, H=64, idx_fmt="fp8",
+                           kv_fmt="fp8", kv_groups=1),
+    "fp8r_h64_mtp2": dict(seed=28, B=2, n_q=2, seq_lens=[2200, 333], top_k=300, H=64, idx_fmt="fp8",
+                          kv_fmt="fp8r", kv_groups=4),
     # more chunks than one round of the chip: the XCD-local block layout
     "xcd_local_ragged": dict(seed=24, B=24, n_q=1, seq_lens=[49152, 20001, 33333, 40960, 47000, 25000, 36000, 44444,
                                                               30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,
