@@ -80,6 +80,15 @@ const char* li_version(void);
 const char* li_last_error(void);
 
 /*
+ * Test hook (not for production use): the number of polls (about 64 cycles of
+ * sleep each) a cross-workgroup exchange wait of li_score_topk makes before it
+ * gives up and takes its exact fallback; default 20000, a negative value
+ * restores the default.  Lowering it forces the fallbacks, which changes
+ * timing only, never results.  Process-wide, read at each call.
+ */
+void li_set_exchange_patience(int32_t polls);
+
+/*
  * Bytes of workspace li_score_topk needs for this geometry.  max_pages bounds
  * every L_b (L_b <= max_pages*64).  Returns 0 for invalid arguments.
  */

@@ -18,6 +18,7 @@ import torch
 
 __all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LI_FP8_ROPE_BF16", "LiError",
            "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
+           "li_set_exchange_patience",
            "li_cache_append"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,7 @@ LI_BF16, LI_FP8, LI_MXFP8, LI_FP8_ROPE_BF16 = 0, 1, 2, 3
 LI_OK = 0
 _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKSPACE", -4: "LI_ERR_HIP"}
 
-EXPORTS = ["li_version", "li_last_error", "li_score_topk_workspace_size", "li_workspace_zero", "li_score_topk",
+EXPORTS = ["li_version", "li_last_error", "li_set_exchange_patience", "li_score_topk_workspace_size", "li_workspace_zero", "li_score_topk",
            "sfa_workspace_size", "sfa_decode", "sfa_prefill", "li_quantize_mxfp8", "li_cache_append"]
 
 
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.li_version.argtypes = []
         L.li_last_error.restype = ctypes.c_char_p
         L.li_last_error.argtypes = []
+        L.li_set_exchange_patience.restype = None
+        L.li_set_exchange_patience.argtypes = [i32]
         L.li_score_topk_workspace_size.restype = sz
         L.li_score_topk_workspace_size.argtypes = [i32, i32, i32, i32]
         L.li_workspace_zero.restype = i32
@@ -101,6 +104,12 @@ def li_score_topk_workspace_size(num_seqs: int, q_per_seq: int, max_pages: int, 
 
 def sfa_workspace_size(num_tokens: int, num_heads: int, top_k: int) -> int:
     return int(lib().sfa_workspace_size(num_tokens, num_heads, top_k))
+
+
+def li_set_exchange_patience(polls: int):
+    """Test hook: polls an indexer exchange wait makes before it takes its exact
+    fallback (negative = the default)."""
+    lib().li_set_exchange_patience(int(polls))
 
 
 def li_workspace_zero(ws: torch.Tensor, stream=None):

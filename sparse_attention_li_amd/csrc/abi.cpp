@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -72,16 +73,12 @@ IdxLayout idx_layout(int B, int n_q, bool fp8, int max_pages) {
   return l;
 }
 
-// Polls an exchange wait makes before giving up (a test hook can lower it
-// through LI_SPIN_MAX to exercise the fallbacks).
-int spin_max() {
-  const char* e = getenv("LI_SPIN_MAX");
-  if (e && *e) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= 0 && v < (1L << 30)) return (int)v;
-  }
-  return 20000;
-}
+// Polls an exchange wait makes before giving up.  Only the test hook
+// li_set_exchange_patience changes it (to force the exact fallbacks).
+constexpr int kDefaultPatience = 20000;
+std::atomic<int> g_patience{kDefaultPatience};
+
+int spin_max() { return g_patience.load(std::memory_order_relaxed); }
 
 // Splits of the index row so that about one workgroup per CU is busy (an
 // attention workgroup fills a CU: one wave per SIMD).  bf16 workgroups hold
@@ -122,6 +119,10 @@ extern "C" {
 const char* li_version(void) { return "sparse_li 0.1.0 (gfx950)"; }
 
 const char* li_last_error(void) { return g_err; }
+
+void li_set_exchange_patience(int32_t polls) {
+  g_patience.store(polls < 0 || polls >= (1 << 30) ? kDefaultPatience : polls, std::memory_order_relaxed);
+}
 
 size_t li_score_topk_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t top_k) {
   if (num_seqs <= 0 || q_per_seq <= 0 || max_pages <= 0 || top_k <= 0) return 0;

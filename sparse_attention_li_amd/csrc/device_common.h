@@ -107,6 +107,34 @@ __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uin
   return oa + ia - a;
 }
 
+// N exclusive scans of 32-bit values with one pair of barriers.  s_tmp needs
+// N*blockDim.x/64 entries.  pre[i] receives the exclusive prefix of v[i],
+// tot[i] its block total (every thread).
+template <int N>
+__device__ __forceinline__ void block_excl_scan_n(const uint32_t (&v)[N], uint32_t* s_tmp, uint32_t (&pre)[N],
+                                                  uint32_t (&tot)[N]) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  uint32_t incl[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) incl[i] = wave_incl_scan(v[i]);
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i) s_tmp[i * nw + wid] = incl[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    uint32_t o = 0, t = 0;
+    for (int w = 0; w < nw; ++w) {
+      const uint32_t x = s_tmp[i * nw + w];
+      o += (w < wid) ? x : 0u;
+      t += x;
+    }
+    pre[i] = o + incl[i] - v[i];
+    tot[i] = t;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- radix select
 // Finds the k-th largest key (1 <= k <= N) among N <= PER*blockDim.x keys
 // given by get(i) (any values, 0 included).  On return every thread
@@ -260,17 +288,26 @@ __device__ uint32_t wave_radix_select(Get get, int N, int k, uint32_t* s_hist, i
 }
 
 // The same selection for inputs too large to hold in registers (rare
-// fallback paths): four 8-bit passes, each streaming all N keys through get().
+// fallback paths): four 8-bit passes, each streaming all N keys through get()
+// with eight reads per thread in flight.
 template <class Get>
 __device__ uint32_t block_radix_select_big(Get get, int N, int k, uint32_t* s_hist, uint32_t* s_sel, int& n_greater) {
+  constexpr int LPT = 8;
   uint32_t prefix = 0, mask = 0;
   uint32_t remaining = (uint32_t)k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) s_hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < N; i += blockDim.x) {
-      const uint32_t key = get(i);
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+    for (int i0 = threadIdx.x; i0 < N; i0 += LPT * (int)blockDim.x) {
+      uint32_t key[LPT];
+#pragma unroll
+      for (int r = 0; r < LPT; ++r) {
+        const int i = i0 + r * (int)blockDim.x;
+        key[r] = i < N ? get(i) : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < LPT; ++r)
+        if (i0 + r * (int)blockDim.x < N && (key[r] & mask) == prefix) atomicAdd(&s_hist[(key[r] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (threadIdx.x < kWave) {

@@ -85,7 +85,7 @@ struct IdxSmem {
   uint32_t mm[NQ][NW][2];                // per-wave min / max valid key
   uint32_t ref[NQ][2];                   // [lo, hi) of this chunk
   uint32_t sel[4];
-  uint32_t scan[16];
+  uint32_t scan[3 * NW];
   uint32_t flag[4];
   uint32_t next_tile;
 };
@@ -618,21 +618,24 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
   for (int j = 0; j < NQ; ++j) {
     if (vis[j] <= K) continue;
     const size_t tok = (size_t)(t0 + j);
-    const uint32_t na_i = cnt_v[j] & 0xffffu, nb_i = cnt_v[j] >> 16;
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan(cnt_v[j], sm.scan, tot);
+    // A chunk's two counts fit 16 bits each (<= CHUNK), but the request's
+    // band can hold every position of the request (scores that rise with
+    // position put each chunk's bracket at a different key): the prefixes over
+    // the chunks are taken as separate 32-bit scans.
+    const uint32_t cv[2] = {cnt_v[j] & 0xffffu, cnt_v[j] >> 16};  // keys >= hi, band keys (0 past n_chunks)
+    uint32_t cpre[2], ctot[2];
+    block_excl_scan_n<2>(cv, sm.scan, cpre, ctot);
     if (tid < n_chunks) {
-      sm.abase[tid] = pre & 0xffffu;
-      sm.cbase[tid] = pre >> 16;
-      sm.nabove[tid] = na_i;
+      sm.abase[tid] = cpre[0];
+      sm.cbase[tid] = cpre[1];
+      sm.nabove[tid] = cv[0];
     }
     if (tid == 0) {
-      sm.abase[n_chunks] = tot & 0xffffu;
-      sm.cbase[n_chunks] = tot >> 16;
+      sm.abase[n_chunks] = ctot[0];
+      sm.cbase[n_chunks] = ctot[1];
     }
-    (void)nb_i;
     __syncthreads();
-    const uint32_t A = tot & 0xffffu, NB = tot >> 16;
+    const uint32_t A = ctot[0], NB = ctot[1];
     const int need = K - (int)A;  // >= 1: fewer than K keys reach hi
     const bool in_lds = NB <= (uint32_t)kBandCap;
     auto gaddr = [&](int i, uint32_t sl) { return (tok * ncm + i) * CHUNK + sl; };
@@ -701,11 +704,21 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
 
     if (mode == kModeNormal) {
       // band entries before this chunk: how many are > tau, how many tie
+      // (from global memory: eight reads per thread in flight)
       uint32_t gt = 0, eq = 0;
-      for (int f = tid; f < (int)sm.cbase[c]; f += THREADS) {
-        const uint32_t key = key_at(f);
-        gt += key > tau ? 1u : 0u;
-        eq += key == tau ? 1u : 0u;
+      const int cb = (int)sm.cbase[c];
+      constexpr int LPT = 8;
+#pragma unroll 1
+      for (int f0 = tid; f0 < cb; f0 += LPT * THREADS) {
+        uint32_t kv[LPT];
+#pragma unroll
+        for (int r = 0; r < LPT; ++r) kv[r] = f0 + r * THREADS < cb ? key_at(f0 + r * THREADS) : 0u;
+#pragma unroll
+        for (int r = 0; r < LPT; ++r) {
+          const bool in = f0 + r * THREADS < cb;
+          gt += (in && kv[r] > tau) ? 1u : 0u;
+          eq += (in && kv[r] == tau) ? 1u : 0u;
+        }
       }
       // own keys in position order: selected for certain (>= hi, or in the
       // band and > tau) or tied at tau
@@ -717,11 +730,13 @@ __device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ
         nd += (kk[i] >= hi_ref[j] || (band && kk[i] > tau)) ? 1u : 0u;
         nt += (band && kk[i] == tau) ? 1u : 0u;
       }
-      // one scan: totals of the earlier chunks' band, prefixes of this chunk's
-      // keys (every count <= the band or the chunk, < 2^16)
-      uint32_t before, pre, tot_pre;
-      block_excl_scan2(gt | (eq << 16), nd | (nt << 16), sm.scan, before, pre, tot_pre);
-      const uint32_t gt_before = before & 0xffffu, eq_before = before >> 16;
+      // one scan: totals of the earlier chunks' band (32 bits each: the band
+      // may hold most of the request), prefixes of this chunk's keys (packed:
+      // both <= CHUNK < 2^16)
+      const uint32_t sv[3] = {gt, eq, nd | (nt << 16)};
+      uint32_t spre[3], stot[3];
+      block_excl_scan_n<3>(sv, sm.scan, spre, stot);
+      const uint32_t gt_before = stot[0], eq_before = stot[1], pre = spre[2];
       const uint32_t avail = ties > eq_before ? ties - eq_before : 0u;  // ties left for this chunk
       uint32_t tr = pre >> 16;                                            // ties of this chunk before my keys
       uint32_t o = sm.abase[c] + gt_before + min(ties, eq_before) + (pre & 0xffffu) + min(avail, tr);

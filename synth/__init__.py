@@ -9,7 +9,8 @@ branch: a 64-head x 128-d lightning indexer over a paged key cache, Top-K
 selection, and MLA attention over a 512 + 64 latent cache shared by all heads.
 Values are drawn so that indexer scores are exact in fp32 under any summation
 order: q and k are integers in [-4, 4], head weights lie on the 1/32 grid of
-(0, 1], FP8 key block scales are 1/2 or 1.  MLA queries and latent rows are
+(0, 1] (or of [-1, 1] without 0 for the signed variant), FP8 key block scales
+are 1/2 or 1.  MLA queries and latent rows are
 N(0, 1) rounded to bf16 (or E4M3 with amax/448 scales for the FP8 cache).
 """
 from __future__ import annotations
@@ -53,6 +54,7 @@ def lib():
         sigs = {
             "synth_idxq_int": [u64, i64, i64, vp],
             "synth_w": [u64, i64, i64, vp],
+            "synth_w_signed": [u64, i64, i64, vp],
             "synth_int_to_bf16": [vp, i64, vp],
             "synth_mx_encode_int": [vp, i64, vp, vp],
             "synth_idxk_int": [u64, i64, i64, i64, vp],
@@ -102,12 +104,13 @@ class Case:
     sm_scale: float = 1.0 / 24.0
     extra_pages: int = 0
     permute_pages: bool = True
+    signed_w: bool = False
     _bt: np.ndarray | None = field(default=None, repr=False)
 
     def __post_init__(self):
         self.seq_lens = np.asarray(self.seq_lens, dtype=np.int32)
         assert self.seq_lens.shape == (self.B,)
-        assert (self.seq_lens >= self.n_q).all()
+        assert (self.seq_lens >= 0).all()
 
     # ---- geometry ----
     @property
@@ -131,7 +134,7 @@ class Case:
         return int(self.seq_lens[b]) - self.n_q + j
 
     def visible(self, t: int) -> int:
-        return self.token_pos(t) + 1
+        return max(0, self.token_pos(t) + 1)
 
     def block_table(self) -> np.ndarray:
         """[B, max_pages] int32; physical pages are a seeded random permutation
@@ -171,7 +174,7 @@ class Case:
     def w(self, t0: int = 0, nt: int | None = None) -> np.ndarray:
         nt = self.T - t0 if nt is None else nt
         out = np.empty((nt, H_IDX), dtype=np.float32)
-        lib().synth_w(self.seed, t0, nt, _p(out))
+        (lib().synth_w_signed if self.signed_w else lib().synth_w)(self.seed, t0, nt, _p(out))
         return out
 
     def k_int(self, b: int, s0: int = 0, s1: int | None = None) -> np.ndarray:

@@ -109,6 +109,19 @@ void synth_w(uint64_t seed, int64_t t0, int64_t nt, float* out) {
   }
 }
 
+/* Head weights of either sign: +-(floor(32u)+1)/32, the sign from the low
+ * bit of the same draw (the magnitude uses the high half).  The head weight is
+ * a projection output, so scores may be negative; on the 1/32 grid they stay
+ * exact in fp32. */
+void synth_w_signed(uint64_t seed, int64_t t0, int64_t nt, float* out) {
+  uint64_t base = stream_base(seed, ST_W);
+  for (int64_t i = 0; i < nt * 64; ++i) {
+    uint64_t u = draw(base, (uint64_t)(t0 * 64 + i));
+    double m = (double)((u >> 32) % 32u + 1u) / 32.0;
+    out[i] = (float)((u & 1u) ? -m : m);
+  }
+}
+
 /* bf16 bits of small integers (exact). */
 void synth_int_to_bf16(const int8_t* in, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne((float)in[i]);

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     src = open(os.path.join(ROOT, "include", "sparse_li.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|li_status)\s+(\w+)\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|li_status|void)\s+(\w+)\(", src, re.M)))
 
 
 def test_every_declared_symbol_is_exported():

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_inputs import GpuCase, rel_err
+from tests.gpu_inputs import GpuCase, encode_indexer_int, load_indexer, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,22 @@ SMALL = {
                                                            30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,
                                                            48000, 23000, 35000, 42000, 29000, 46000, 39000, 31000],
                           top_k=2048, H=16, idx_fmt="mxfp8", kv_fmt="fp8"),
+    # head weights of either sign: negative scores, ordered by their keys
+    "signed_bf16": dict(seed=30, B=3, n_q=1, seq_lens=[900, 5000, 2049], top_k=512, H=32, signed_w=True),
+    "signed_k_deep": dict(seed=31, B=2, n_q=1, seq_lens=[3000, 2500], top_k=2048, H=16, signed_w=True),
+    "signed_fp8_mtp2": dict(seed=32, B=2, n_q=2, seq_lens=[4097, 1300], top_k=300, H=64, idx_fmt="fp8",
+                            kv_fmt="fp8", kv_groups=5, signed_w=True),
+    "signed_mxk": dict(seed=33, B=3, n_q=1, seq_lens=[700, 2600, 4100], top_k=1500, H=32, idx_fmt="mxfp8",
+                       kv_fmt="fp8", kv_groups=1, signed_w=True),
+    "signed_xcd_local_fp8": dict(seed=34, B=24, n_q=1, seq_lens=[20000 + 1237 * b for b in range(24)], top_k=2048,
+                                 H=16, idx_fmt="fp8", kv_fmt="fp8", signed_w=True),
+    "signed_prefill": dict(seed=35, B=1, n_q=40, seq_lens=[3000], top_k=256, H=16, signed_w=True),
+    "signed_prefill_deep": dict(seed=36, B=1, n_q=12, seq_lens=[2600], top_k=2048, H=32, signed_w=True),
+    "signed_prefill_compactions": dict(seed=37, B=1, n_q=12, seq_lens=[9000], top_k=512, H=64, signed_w=True),
+    # requests with no cached position: the row is all -1, out 0, lse -inf
+    "empty_requests": dict(seed=38, B=3, n_q=1, seq_lens=[0, 1500, 0], top_k=256, H=16),
+    "empty_requests_fp8_mtp2": dict(seed=39, B=3, n_q=2, seq_lens=[2100, 0, 700], top_k=300, H=128, idx_fmt="fp8",
+                                    kv_fmt="fp8", kv_groups=5),
     # prefill chunks (many causal queries per request)
     "prefill_ragged": dict(seed=19, B=1, n_q=37, seq_lens=[300], top_k=64, H=16),
     "prefill_k_gt_visible": dict(seed=20, B=2, n_q=9, seq_lens=[40, 200], top_k=128, H=32),
@@ -182,14 +198,14 @@ def test_attention_all_positions_equals_dense(li):
 
 
 def test_decode_b32_ctx32k_sampled(li):
-    """Full-size headline workload, same launch as the benchmark; sampled tokens
+    """Full-size headline workload, same launch as the benchmark; every token
     checked end to end against the oracle."""
     case = synth.workload("decode_b32_ctx32k")
     g = GpuCase(case)
     idx = g.score_topk(li)
     out, lse = g.attend(li, idx)
     torch.cuda.synchronize()
-    tokens = [0, 13, 31]
+    tokens = list(range(case.T))
     ores = oracle.run_tokens(case, tokens)
     idx = idx.cpu().numpy()
     _check_indices(case, idx, tokens, ores)
@@ -214,12 +230,19 @@ def test_repeated_calls_identical_many_chunks(li):
 
 @pytest.mark.parametrize("spin", [0, 3])
 @pytest.mark.parametrize("name", ["ragged3", "mtp2", "k2048", "fp8_g5_mtp2", "xcd_local_fp8"])
-def test_exchange_fallbacks_stay_exact(li, monkeypatch, name, spin):
+def test_exchange_fallbacks_stay_exact(li, name, spin):
     """The decode indexer's cross-workgroup exchanges with (almost) no patience:
     most waits time out, so workgroups publish every key, give up their share
     and leave the whole request to the last one to arrive.  Indices must still
     equal the oracle's, and the exchange state must be left reset."""
-    monkeypatch.setenv("LI_SPIN_MAX", str(spin))
+    li.li_set_exchange_patience(spin)
+    try:
+        _fallback_case(li, name)
+    finally:
+        li.li_set_exchange_patience(-1)
+
+
+def _fallback_case(li, name):
     case = synth.Case(**SMALL[name])
     g = GpuCase(case, attention=False)
     ws = torch.zeros(li.li_score_topk_workspace_size(case.B, case.n_q, case.max_pages, case.top_k),
@@ -261,6 +284,88 @@ def test_positional_trend_band_beyond_lds(li):
     assert idx[0].min() > L // 2  # the trend really puts the selection in the last chunks
 
 
+def _trend_keys(L: int, rising: bool, seed: int) -> np.ndarray:
+    """Key rows whose score against an all-ones query grows (or falls) with
+    position: ones in the first m(s) = 128 s / L entries plus sparse +-1
+    noise, all integers in [-4, 4]."""
+    rng = np.random.default_rng(seed)
+    s = np.arange(L) if rising else np.arange(L)[::-1]
+    m = (s * 128) // L
+    k = (np.arange(128)[None, :] < m[:, None]).astype(np.int8)
+    k += (rng.integers(-1, 2, size=(L, 128)) * (rng.random((L, 128)) < 0.05)).astype(np.int8)
+    return k
+
+
+@pytest.mark.parametrize("kind", ["trend", "zero_query"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_band_beyond_16_bits(li, fmt, kind):
+    """131,072 positions per request whose scores rise (request 0) or fall
+    (request 1) with position, or a zero query (every score equal): the band
+    between the chunks' bracketing keys holds more than 65,535 entries
+    (modelled on the CPU in test_band_model.py), so its counts and offsets
+    must be 32-bit.  Indices must equal the oracle's."""
+    L, K = 131072, 2048
+    case = synth.Case(seed=40, B=2, n_q=1, seq_lens=[L, L], top_k=K, H=16, idx_fmt=fmt,
+                      kv_fmt="fp8" if fmt != "bf16" else "bf16")
+    g = GpuCase(case, attention=False)
+    q_int = np.zeros((2, 64, 128), np.int8) if kind == "zero_query" else np.ones((2, 64, 128), np.int8)
+    w = np.full((2, 64), 0.5, np.float32)
+    k_int = [_trend_keys(L, True, 1), _trend_keys(L, False, 2)]
+    q, qs, ks = encode_indexer_int(case, q_int, k_int)
+    load_indexer(g, q, qs, w, ks)
+    idx = g.score_topk(li).cpu().numpy()
+    q_fmt = "bf16" if fmt == "bf16" else "fp8"
+    for b in range(2):
+        if kind == "zero_query":
+            assert (idx[b] == np.arange(K)).all()
+            continue
+        sc = oracle.index_scores(q[b], w[b], ks[b][0], L, q_fmt=q_fmt, q_scales=None if qs is None else qs[b],
+                                 k_fmt=fmt, k_scales=ks[b][1])
+        ridx, n = oracle.topk(sc, K)
+        assert (idx[b] == np.sort(ridx[:n])).all(), f"request {b}"
+        # the trend really spreads the chunk brackets (far beyond the first / last chunks)
+        assert (idx[b].min() > L // 2) if b == 0 else (idx[b].max() < L // 2)
+
+
+@pytest.mark.parametrize("spin", [0, 3])
+def test_band_beyond_16_bits_with_fallbacks(li, spin):
+    """The rising-trend request of 131,072 positions with (almost) no patience
+    in the exchanges: timed-out workgroups publish every key as band and the
+    last to arrive writes the whole request from the lists; still exact."""
+    L, K = 131072, 2048
+    case = synth.Case(seed=42, B=1, n_q=1, seq_lens=[L], top_k=K, H=16)
+    g = GpuCase(case, attention=False)
+    q, qs, ks = encode_indexer_int(case, np.ones((1, 64, 128), np.int8), [_trend_keys(L, True, 3)])
+    w = np.full((1, 64), 0.5, np.float32)
+    load_indexer(g, q, qs, w, ks)
+    sc = oracle.index_scores(q[0], w[0], ks[0][0], L)
+    ridx, n = oracle.topk(sc, K)
+    li.li_set_exchange_patience(spin)
+    try:
+        for _ in range(2):
+            idx = g.score_topk(li).cpu().numpy()
+            assert (idx[0] == np.sort(ridx[:n])).all()
+    finally:
+        li.li_set_exchange_patience(-1)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_two_token_call_equals_one_token_calls(li, fmt):
+    """Token j of a two-token (draft-and-verify) call sees L - 1 + j positions:
+    it must select what a one-token call over the same cache with the length
+    L - 1 + j selects."""
+    case = synth.Case(seed=41, B=3, n_q=2, seq_lens=[5000, 2050, 9001], top_k=700, H=16, idx_fmt=fmt,
+                      kv_fmt="fp8" if fmt != "bf16" else "bf16", signed_w=True)
+    g = GpuCase(case, attention=False)
+    both = g.score_topk(li).cpu().numpy()
+    for j in range(2):
+        sl = (g.seq_lens - (1 - j)).contiguous()
+        one = li.li_score_topk(g.q[j::2].contiguous(), g.w[j::2].contiguous(), g.k_pool, sl, g.block_table,
+                               case.top_k, q_scales=None if g.q_scales is None else g.q_scales[j::2].contiguous(),
+                               k_scales=g.k_scales).cpu().numpy()
+        assert (one == both[j::2]).all(), f"token {j}"
+
+
 def test_prefill_all_equal_scores(li):
     case = synth.Case(seed=22, B=1, n_q=8, seq_lens=[5000], top_k=700, H=16)
     g = GpuCase(case, attention=False)
@@ -271,26 +376,31 @@ def test_prefill_all_equal_scores(li):
 
 def test_prefill_4k_on_64k_sampled(li):
     """Full-size prefill chunk: 4096 causal queries on a 65536-token cache;
-    sampled queries (first, last and spread) checked against the oracle."""
+    stratified queries checked against the oracle."""
     case = synth.workload("prefill_4k_on_64k")
     g = GpuCase(case)
     idx = g.score_topk(li)
     out, lse = g.attend(li, idx, prefill=True)
     torch.cuda.synchronize()
-    tokens = [0, 1, 1365, 2730, 4095]
-    ores = oracle.run_tokens(case, tokens)
+    # indices of 258 stratified queries (every 16th, the first and the last),
+    # attention of every 64th
+    tokens = sorted(set(range(0, case.T, 16)) | {1, case.T - 1})
+    ores = oracle.run_tokens(case, tokens, with_attn=False)
     _check_indices(case, idx.cpu().numpy(), tokens, ores)
-    _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), tokens, ores)
+    atok = sorted(set(range(0, case.T, 64)) | {case.T - 1})
+    ores = oracle.run_tokens(case, atok)
+    _check_attention(case, out.float().cpu().numpy(), lse.cpu().numpy(), atok, ores)
 
 
 def test_decode_b64_var_fp8_sampled(li):
     """Full-size FP8 workload (64 requests of 4K..128K positions, MXFP8 indexer
     query, FP8 keys and latent), same launches as a decode step; sampled
-    requests (shortest, longest, first, last) checked end to end.  Latent rows
+    requests (shortest, longest, first, last and every fifth) checked end to end.  Latent rows
     are generated for the sampled requests only."""
     case = synth.workload("decode_b64_var_fp8")
     L = case.seq_lens
-    tokens = sorted({0, case.B - 1, int(np.argmin(L)), int(np.argmax(L))})
+    tokens = sorted({0, case.B - 1, int(np.argmin(L)), int(np.argmax(L))} | set(range(3, case.B, 5)))
+    assert len(tokens) >= 16
     g = GpuCase(case, latent_requests=tokens)
     idx = g.score_topk(li)
     out, lse = g.attend(li, idx)
@@ -307,7 +417,7 @@ def test_decode_b64_var_mxfp8_keys_sampled(li):
     workload above)."""
     case = synth.workload("decode_b64_var_mxfp8")
     L = case.seq_lens
-    tokens = sorted({0, case.B - 1, int(np.argmin(L)), int(np.argmax(L))})
+    tokens = sorted({0, case.B - 1, int(np.argmin(L)), int(np.argmax(L))} | set(range(2, case.B, 5)))
     g = GpuCase(case, attention=False)
     assert g.k_scales.dtype == torch.uint8 and g.k_scales.shape[-1] == 4
     idx = g.score_topk(li)
@@ -319,9 +429,9 @@ def test_decode_b64_var_mxfp8_keys_sampled(li):
 def test_decode_b128_ctx128k_mtp2_sampled(li):
     """Full-size two-token verification workload: 128 requests x 131072
     positions, FP8 keys, latent FP8 with one scale per 128-wide tile; both
-    tokens of the first and last request checked end to end."""
+    tokens of eight requests spread over the batch checked end to end."""
     case = synth.workload("decode_b128_ctx128k_mtp2")
-    reqs = [0, case.B - 1]
+    reqs = [0, 17, 38, 55, 64, 90, 111, case.B - 1]
     g = GpuCase(case, latent_requests=reqs)
     idx = g.score_topk(li)
     out, lse = g.attend(li, idx)

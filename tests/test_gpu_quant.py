@@ -41,6 +41,27 @@ def test_mxfp8_matches_oracle(li):
     assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:3]}: gpu {got[tuple(bad[0])]} oracle {rc[tuple(bad[0])]}"
 
 
+def test_mxfp8_tiny_groups_hold_least_scale(li):
+    """Groups with subnormal or tiny maxima (below 2^-119): the E8M0 scale
+    holds at code 0 (2^-127) and codes are x * 2^127, bit-exact against the
+    oracle."""
+    rng = np.random.default_rng(41)
+    n = 64
+    bits = rng.integers(0, 0x80, (n, 32)).astype(np.uint16)              # subnormal magnitudes
+    bits |= rng.integers(0, 2, (n, 32)).astype(np.uint16) << 15          # both signs
+    e_field = rng.integers(1, 12, n).astype(np.uint16)                   # amax 2^-126 .. 2^-116
+    pos = rng.integers(0, 32, n)
+    bits[np.arange(n) // 2 * 2, pos[np.arange(n) // 2 * 2]] = e_field[np.arange(n) // 2 * 2] << 7
+    bits[7] = 0x0001                                                     # 2^-133 everywhere
+    xt = torch.from_numpy(bits.view(np.int16)).cuda()
+    codes, scales = li.li_quantize_mxfp8(xt.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant_mxfp8(bits)
+    assert (rs <= 3).all() and (rs == 0).sum() > n // 4  # the clamp is reached
+    assert (scales.cpu().numpy() == rs).all()
+    assert (codes.cpu().numpy() == rc).all()
+
+
 def _pools(rng, num_pages, fp8_k, fp8_kv, groups):
     k = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 256), dtype=np.uint8)).cuda()
     kv = torch.from_numpy(rng.integers(0, 256, (num_pages, 64, 1152), dtype=np.uint8)).cuda()

@@ -396,3 +396,31 @@ def test_quant_fp8_rows_per_token_and_per_tile():
                     got = oracle.e4m3(int(codes[r, lo + i]))
                     assert abs(abs(got) - min(abs(q[i]), 448.0)) == np.abs(np.abs(vals) - min(abs(q[i]), 448.0)).min()
                     assert got == 0 or np.sign(got) == np.sign(q[i])
+
+
+def test_quant_mxfp8_e8m0_clamp_on_tiny_groups():
+    """Groups whose largest magnitude is below 2^-119 (bf16 subnormals and the
+    smallest normals): floor(log2 amax) - 8 falls below E8M0's least exponent
+    -127 (OCP Microscaling v1.0: E8M0 spans 2^-127 .. 2^127), so the scale
+    holds at code 0 and the elements are x * 2^127 rounded to E4M3.  Reference
+    codes come from torch's float8 cast of the exact products."""
+    rng = np.random.default_rng(11)
+    groups = []
+    # (bf16 bit patterns of one group, expected E8M0 code)
+    groups.append((np.full(32, 0x0001, np.uint16), 0))                     # every element 2^-133
+    sub = rng.integers(1, 0x80, 32).astype(np.uint16) | (rng.integers(0, 2, 32).astype(np.uint16) << 15)
+    groups.append((sub, 0))                                                # mixed subnormals, both signs
+    for e_field, code in [(7, 0), (8, 0), (9, 1), (10, 2)]:
+        # amax = 2^(e_field - 127) (a normal bf16); floor(log2 amax) - 8 + 127 = e_field - 8
+        g = rng.integers(0, 0x80, 32).astype(np.uint16)                    # subnormal fill
+        g[int(rng.integers(0, 32))] = np.uint16(e_field << 7)
+        groups.append((g, code))
+        assert code == max(e_field - 8, 0)
+    x = np.stack([g for g, _ in groups])
+    codes, scales = oracle.quant_mxfp8(x)
+    assert list(scales[:, 0]) == [c for _, c in groups]
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy()
+    X = np.array([2.0 ** (c - 127) for _, c in groups])[:, None]
+    ref = torch.from_numpy(xf / X).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (codes == ref).all()
+    assert (codes[0] == 0x08).all()  # 2^-133 * 2^127 = 2^-6, E4M3's least normal
