@@ -138,6 +138,31 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
                         const void* k_scales, int32_t top_k, int32_t* idx_out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Bytes of the library-owned exchange workspace of li_score_topk_noalloc, per GPU. */
+#define LI_NOALLOC_WORKSPACE_MAX (128u << 20)
+
+/*
+ * li_score_topk_noalloc -- li_score_topk without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc).  Same arguments,
+ * layouts, results and errors as li_score_topk, minus the workspace.  It
+ * allocates nothing: the exchange workspace is a device array of
+ * LI_NOALLOC_WORKSPACE_MAX bytes inside the library, one per GPU, held until
+ * the process ends.
+ *   - Geometries whose li_score_topk_workspace_size exceeds that size return
+ *     LI_ERR_UNSUPPORTED (e.g. 128 requests x 2 tokens x 131072 positions).
+ *   - The first call on a device also clears the array, with a fill kernel
+ *     enqueued on `stream` before the indexer.
+ *   - Every call on one GPU uses the same array (each call leaves its
+ *     counters zero for the next): calls that overlap in time on one GPU --
+ *     other streams, other host threads -- race and give wrong results.
+ */
+li_status li_score_topk_noalloc(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens,
+                                const int32_t* block_table, int32_t max_pages, int32_t num_pages, int32_t q_dtype,
+                                const void* q, const uint8_t* q_scales, const float* w, int32_t k_dtype,
+                                const void* k_cache, const void* k_scales, int32_t top_k, int32_t* idx_out,
+                                void* stream);
+
 /*
  * Bytes of workspace sfa_decode / sfa_prefill need (split partial results).
  */

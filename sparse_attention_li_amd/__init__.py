@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LI_FP8_ROPE_BF16", "LiError",
            "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
-           "li_set_exchange_patience",
+           "li_set_exchange_patience", "li_score_topk_noalloc",
            "li_cache_append"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,8 @@ LI_BF16, LI_FP8, LI_MXFP8, LI_FP8_ROPE_BF16 = 0, 1, 2, 3
 LI_OK = 0
 _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKSPACE", -4: "LI_ERR_HIP"}
 
-EXPORTS = ["li_version", "li_last_error", "li_set_exchange_patience", "li_score_topk_workspace_size", "li_workspace_zero", "li_score_topk",
+EXPORTS = ["li_version", "li_last_error", "li_set_exchange_patience", "li_score_topk_workspace_size",
+           "li_score_topk_noalloc", "li_workspace_zero", "li_score_topk",
            "sfa_workspace_size", "sfa_decode", "sfa_prefill", "li_quantize_mxfp8", "li_cache_append"]
 
 
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.li_workspace_zero.argtypes = [vp, sz, vp]
         L.li_score_topk.restype = i32
         L.li_score_topk.argtypes = [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp, sz, vp]
+        L.li_score_topk_noalloc.restype = i32
+        L.li_score_topk_noalloc.argtypes = [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp]
         L.sfa_workspace_size.restype = sz
         L.sfa_workspace_size.argtypes = [i32, i32, i32]
         sfa_args = [i32, i32, vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
@@ -156,6 +159,23 @@ def li_score_topk(q: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, seq_l
                              _ptr(q_scales), _ptr(w), k_dtype, _ptr(k_cache), _ptr(k_scales), top_k,
                              _ptr(idx_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream))
+    _check(st)
+    return idx_out
+
+
+def li_score_topk_noalloc(q: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, seq_lens: torch.Tensor,
+                          block_table: torch.Tensor, top_k: int, idx_out: torch.Tensor,
+                          q_scales: torch.Tensor | None = None, k_scales: torch.Tensor | None = None, stream=None):
+    """li_score_topk with the library's own exchange workspace (no allocation by
+    the library or here): the caller passes idx_out [T,top_k] int32."""
+    B = seq_lens.shape[0]
+    T = q.shape[0]
+    if T % B:
+        raise ValueError("q.shape[0] must be a multiple of len(seq_lens)")
+    k_dtype = LI_MXFP8 if k_scales is not None and k_scales.dtype == torch.uint8 else _dtype_of(k_cache)
+    st = lib().li_score_topk_noalloc(B, T // B, _ptr(seq_lens), _ptr(block_table), block_table.shape[1],
+                                     k_cache.shape[0], _dtype_of(q), _ptr(q), _ptr(q_scales), _ptr(w), k_dtype,
+                                     _ptr(k_cache), _ptr(k_scales), top_k, _ptr(idx_out), _stream(stream))
     _check(st)
     return idx_out
 

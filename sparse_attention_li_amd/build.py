@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_li.so")
 
-SOURCES = ["abi.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip"]
+SOURCES = ["abi.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip", "noalloc.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -114,6 +114,14 @@ li_status check_paged(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_le
 
 }  // namespace
 
+li_status sli::report(li_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
 extern "C" {
 
 const char* li_version(void) { return "sparse_li 0.1.0 (gfx950)"; }

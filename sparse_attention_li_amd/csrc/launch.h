@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sparse_li.h"
+
 namespace sli {
 
 constexpr int kCounterStride = 32;     // uint32 words per request (one 128-byte line)
@@ -83,6 +85,9 @@ struct AppendArgs {
   void* kv_cache;     // [num_pages][64][576] bf16 or E4M3
   float* kv_scales;   // [num_pages][64][kv_groups] (FP8)
 };
+
+// Records a failure message for li_last_error() (printf format) and returns s.
+li_status report(li_status s, const char* fmt, ...);
 
 hipError_t launch_mxfp8_quant(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_cache_append(const AppendArgs& a, hipStream_t stream);

@@ -126,3 +126,17 @@ def _call_append(**over):
 def test_cache_append_argument_errors(over, status):
     st, msg = _call_append(**over)
     assert st == status and msg
+
+
+def test_noalloc_rejects_geometries_beyond_its_array():
+    """The allocation-free indexer serves geometries whose exchange workspace
+    fits the library's array and rejects larger ones before touching a device."""
+    L = li.lib()
+    P = ctypes.c_void_p(0x10000)
+    cap = 128 << 20
+    assert L.li_score_topk_workspace_size(32, 1, 512, 2048) <= cap       # 32 x 32K decode
+    assert L.li_score_topk_workspace_size(128, 2, 2048, 2048) > cap      # 128 x 2 tokens x 128K
+    st = L.li_score_topk_noalloc(128, 2, P, P, 2048, 262144, 1, P, P, P, 1, P, P, 2048, P, None)
+    assert st == -2 and b"li_score_topk_noalloc" in L.li_last_error()
+    st = L.li_score_topk_noalloc(0, 1, P, P, 32, 32, 0, P, None, P, 0, P, None, 256, P, None)
+    assert st == -1 and L.li_last_error()
