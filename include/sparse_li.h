@@ -204,6 +204,48 @@ li_status sfa_prefill(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_le
                       size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of workspace li_decode_step needs (q_per_seq 1 or 2); 0 for invalid
+ * arguments.
+ */
+size_t li_decode_step_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t num_heads,
+                                     int32_t top_k);
+
+/*
+ * li_decode_step -- one whole decode step of the sparse-attention path:
+ * li_score_topk followed by sfa_decode on the same stream, as one launch
+ * where the shape allows it.  The pages take every step other than attention
+ * off the decode critical path by fusing the indexer into one operator and
+ * dispatching the layer as one kernel ("Day-0 Inference Adaptation and
+ * Optimization for Hybrid Attention Architectures", sec. 3; "Day0 Inference
+ * Adaptation and Performance Optimization for a Sparse Hybrid Architecture
+ * LLM", sec. 6).
+ *
+ *   Arguments: those of li_score_topk (q_idx = its q) and of sfa_decode (q =
+ *   the MLA query), sharing num_seqs .. num_pages and top_k; idx_out receives
+ *   the index rows and is read back by the attention.
+ *   workspace  li_decode_step_workspace_size(...) bytes, zero before its first
+ *              use (li_workspace_zero); every call leaves it so.  The same
+ *              contract as li_score_topk's workspace; calls that share a
+ *              workspace must not overlap in time.
+ * One launch for bf16 query, keys and latent, q_per_seq = 1, num_heads = 128
+ * and at most one 4096-position chunk per compute unit (num_seqs *
+ * ceil(max_pages * 64 / 4096) <= CUs, <= 64 chunks per request): each
+ * chunk's workgroup scores its chunk, writes its share of the index row, then
+ * runs attention splits of its request once the row is complete and merges
+ * the split partials in the same launch.  Other shapes run li_score_topk and
+ * sfa_decode back to back.  idx_out is identical to li_score_topk's; out and
+ * lse equal sfa_decode's up to the rounding of the split partials (the
+ * fused launch splits the index row differently).
+ */
+li_status li_decode_step(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
+                         int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q_idx,
+                         const uint8_t* q_scales, const float* w, int32_t k_dtype, const void* k_cache,
+                         const void* k_scales, const void* q, int32_t num_heads, int32_t kv_dtype,
+                         const void* kv_cache, const float* kv_scales, int32_t kv_scale_groups, int32_t top_k,
+                         float sm_scale, int32_t* idx_out, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * li_quantize_mxfp8 -- MXFP8 quantisation of bf16 rows, e.g. the indexer
  * query before li_score_topk ("Day-0 Inference Adaptation and Optimization
  * for Hybrid Attention Architectures", sec. 4: MXFP8 indexer query, group 32;

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LI_FP8_ROPE_BF16", "LiError",
            "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
-           "li_set_exchange_patience", "li_score_topk_noalloc",
+           "li_set_exchange_patience", "li_score_topk_noalloc", "li_decode_step", "li_decode_step_workspace_size",
            "li_cache_append"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ LI_OK = 0
 _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKSPACE", -4: "LI_ERR_HIP"}
 
 EXPORTS = ["li_version", "li_last_error", "li_set_exchange_patience", "li_score_topk_workspace_size",
-           "li_score_topk_noalloc", "li_workspace_zero", "li_score_topk",
+           "li_score_topk_noalloc", "li_decode_step", "li_decode_step_workspace_size", "li_workspace_zero", "li_score_topk",
            "sfa_workspace_size", "sfa_decode", "sfa_prefill", "li_quantize_mxfp8", "li_cache_append"]
 
 
@@ -64,6 +64,11 @@ def lib() -> ctypes.CDLL:
         L.li_score_topk.argtypes = [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp, sz, vp]
         L.li_score_topk_noalloc.restype = i32
         L.li_score_topk_noalloc.argtypes = [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp]
+        L.li_decode_step_workspace_size.restype = sz
+        L.li_decode_step_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.li_decode_step.restype = i32
+        L.li_decode_step.argtypes = [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, vp, vp, i32,
+                                     i32, f32, vp, vp, vp, vp, sz, vp]
         L.sfa_workspace_size.restype = sz
         L.sfa_workspace_size.argtypes = [i32, i32, i32]
         sfa_args = [i32, i32, vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
@@ -215,6 +220,44 @@ def sfa_decode(q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None
 def sfa_prefill(q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales=None, **kw):
     """sfa_decode's operation with the launch shape for a prefill chunk."""
     return _sfa(lib().sfa_prefill, q, kv_cache, idx, seq_lens, block_table, sm_scale, kv_scales, **kw)
+
+
+def li_decode_step_workspace_size(num_seqs: int, q_per_seq: int, max_pages: int, num_heads: int, top_k: int) -> int:
+    return int(lib().li_decode_step_workspace_size(num_seqs, q_per_seq, max_pages, num_heads, top_k))
+
+
+def li_decode_step(q_idx: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, q: torch.Tensor,
+                   kv_cache: torch.Tensor, seq_lens: torch.Tensor, block_table: torch.Tensor, top_k: int,
+                   sm_scale: float, q_scales=None, k_scales=None, kv_scales=None, idx_out=None, out=None, lse=None,
+                   workspace=None, stream=None):
+    """The whole decode step (indexer score + Top-K, then sparse MLA attention),
+    one launch where the shape allows.  Returns (idx, out, lse)."""
+    B = seq_lens.shape[0]
+    T, H = q.shape[0], q.shape[1]
+    if T % B or q_idx.shape[0] != T:
+        raise ValueError("q and q_idx must hold the same multiple of len(seq_lens) tokens")
+    n_q = T // B
+    max_pages = block_table.shape[1]
+    if idx_out is None:
+        idx_out = torch.empty((T, top_k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace("step", li_decode_step_workspace_size(B, n_q, max_pages, H, top_k), q.device)
+    k_dtype = LI_MXFP8 if k_scales is not None and k_scales.dtype == torch.uint8 else _dtype_of(k_cache)
+    kv_dtype = _dtype_of(kv_cache)
+    if kv_dtype == LI_FP8 and kv_cache.shape[-1] == 640:
+        kv_dtype = LI_FP8_ROPE_BF16
+    groups = 1 if kv_scales is None else (kv_scales.shape[2] if kv_scales.dim() == 3 else 1)
+    st = lib().li_decode_step(B, n_q, _ptr(seq_lens), _ptr(block_table), max_pages, k_cache.shape[0], _dtype_of(q_idx),
+                              _ptr(q_idx), _ptr(q_scales), _ptr(w), k_dtype, _ptr(k_cache), _ptr(k_scales), _ptr(q), H,
+                              kv_dtype, _ptr(kv_cache), _ptr(kv_scales), groups, top_k, float(sm_scale), _ptr(idx_out),
+                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    _check(st)
+    return idx_out, out, lse
 
 
 def li_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,

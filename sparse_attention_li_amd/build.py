@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_li.so")
 
-SOURCES = ["abi.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip", "noalloc.hip",
+           "decode_step.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -25,7 +26,8 @@ HIP_FLAGS = [
 # awaited by explicit lgkmcnt waits: the compiler does not know such a
 # register is still being written until the wait, so the build scans their
 # assembly for any use of it in between (lds_hazards.py).
-LDS_CHECKED = {"sfa.hip": ("sfa_bf16_kernel",)}
+LDS_CHECKED = {"sfa.hip": ("sfa_bf16_kernel",), "indexer_decode.hip": ("li_decode_kernel",),
+               "decode_step.hip": ("li_step_kernel",)}
 
 
 def check_lds_hazards(src: str, inc: list, kernels: tuple) -> None:

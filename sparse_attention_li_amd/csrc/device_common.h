@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace sli {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -18,6 +21,22 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at max).
+#define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
+
+// Calls f(std::integral_constant<int, J>) for J = 0 .. N-1: the body is
+// instantiated once per J, so everything indexed by J is a constant.
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---------------------------------------------------------------- score keys
 // Order-preserving map from fp32 to uint32: larger float -> larger key.
@@ -133,6 +152,19 @@ __device__ __forceinline__ void block_excl_scan_n(const uint32_t (&v)[N], uint32
     tot[i] = t;
   }
   __syncthreads();
+}
+
+// Block-wide AND of a predicate, with the barrier of __syncthreads_and but
+// on caller-provided LDS (one word per wave), so a kernel's LDS is all its own.
+__device__ __forceinline__ bool block_all(bool p, uint32_t* s_tmp) {
+  const int wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const bool wave_ok = __ballot(!p) == 0ull;
+  if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[wid] = wave_ok ? 1u : 0u;
+  __syncthreads();
+  bool r = true;
+  for (int i = 0; i < nw; ++i) r = r && s_tmp[i] != 0u;
+  __syncthreads();
+  return r;
 }
 
 // ---------------------------------------------------------------- radix select
@@ -437,6 +469,19 @@ __device__ __forceinline__ void xstore64(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint64_t xload64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// 16-byte accesses of data exchanged between the workgroups of one launch,
+// system-coherent like xstore / xload (cache policy sc0 sc1), through a buffer
+// resource over a wave-uniform `base` with a per-lane byte offset < 2 GiB.
+constexpr int kCPolSystem = 1 | 16;  // sc0 | sc1
+__device__ __forceinline__ void xstore128(void* base, uint32_t off, i32x4 v) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCPolSystem);
+}
+__device__ __forceinline__ i32x4 xload128(const void* base, uint32_t off) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCPolSystem);
 }
 
 // Waits until this wave's outstanding vector-memory operations (stores

@@ -1,808 +1,20 @@
-// Fused lightning-indexer score + Top-K for decode (1 or 2 query tokens per
-// request), gfx950.
-//
-// What it computes (pages: "Optimizing Inference for Hybrid Attention LLMs",
-// sec. 3.1; "Day0 Inference Support and Performance Optimization for
-// New-Architecture LLMs", sec. 4): for each query token t of request b and
-// every visible cached position s,
-//     I[t,s] = sum_h w[t,h] * ReLU(q[t,h,:] . k[s,:])        (64 heads x 128)
-// and the min(K, visible) positions with the largest I (ties to the lower
-// position).  Only the indices leave the chip.
-//
-// Decomposition.  One workgroup (4 waves) owns a chunk of CHUNK consecutive
-// positions of one request and all of the request's query tokens, so the key
-// pages are streamed from HBM exactly once.  Per 32-position tile a wave runs
-//     S[head, pos] = q[head, :] . k[pos, :]   on 32x32 MFMA tiles (heads = M),
-// so each lane ends up holding 16 heads of one position and the head
-// reduction sum_h w*ReLU(S) is 16 in-lane FMAs plus one cross-half swap.
-// Scores become order-preserving uint32 keys in LDS; they never reach HBM.
-//
-// Exact selection across the n chunks of a request, every workgroup writing
-// its own chunk's share of the output (kappa = the K-th largest key):
-//   1. chunk c takes a quota R_c with K <= sum R_c < K + n and finds, from
-//      one LDS histogram of its keys, a key interval [lo_c, hi_c) holding
-//      its R_c-th largest key: >= R_c of its keys are >= lo_c and < R_c are
-//      >= hi_c.  Hence lo = min lo_c and hi = max hi_c bracket kappa:
-//      >= sum R_c >= K keys are >= lo, and <= sum (R_c - 1) < K keys are
-//      >= hi.  The quotas follow the chunks' visible positions, so every
-//      bracket sits near the same quantile and the band stays narrow: whole
-//      chunks split K evenly; when the last chunk holds only v < CHUNK of the
-//      vis visible positions it takes floor(K v / vis) (possibly 0: then its
-//      interval is empty below and ends above its largest key) and the others
-//      ceil((K - that) / (n - 1)).  Chunks past the visible ones publish an
-//      empty interval.  Exchange 1 publishes the intervals;
-//   2. keys >= hi are selected for certain; each chunk publishes its count of
-//      them and its "band" keys in [lo, hi) with their positions (exchange 2);
-//   3. every workgroup loads all band keys of the request (a few per cent of
-//      the positions), selects kappa among them exactly (radix select,
-//      need = K - #keys >= hi), counts what the chunks before it select, and
-//      writes its own selected positions at that offset, in position order.
-// The exchanges are arrival counters with bounded waits.  A workgroup whose
-// first wait times out (its request's chunks were not all resident) publishes
-// every key as band, which keeps the result exact; one whose second wait
-// times out leaves its share to the last workgroup to arrive, which then
-// writes the whole request from the published lists.
-#include "device_common.h"
-#include "launch.h"
+// Decode launches of the fused lightning-indexer score + Top-K (the kernel
+// body, its decomposition and its exact cross-chunk selection are described in
+// indexer_decode_body.h), and the workspace fill kernel.
+#include "indexer_decode_body.h"
 
 namespace sli {
 
-typedef __attribute__((address_space(3))) void lds_void;
-#define SLI_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N)&15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
-
-constexpr int kHistBins = 4096;  // LDS histogram that brackets a chunk's R-th largest key
-constexpr int kBandCap = 4096;   // band entries the final select keeps in LDS
-
-// Words of the fixed counter region (one 128-byte line per request, then one
-// line for the whole launch).  Exchange data carries a per-call tag (the
-// launch epoch + 1) in its upper 32 bits, so a reader polls the data itself:
-// no counter, no fence on the common path.  The epoch is one for the whole
-// workspace, so no word left by an earlier call -- for any request and any
-// batch shape -- carries the current tag.  The per-request counters only
-// settle the rare give-up fallback; the launch line counts departing
-// workgroups, and the last one advances the epoch.
-enum : uint32_t { kArrive2 = 0, kDone = 1, kState = 2 };
-enum : uint32_t { kGridDone = 0, kGridEpoch = 1 };
-enum : uint32_t { kStLast = 1u, kStGaveUp = 2u };
-enum : uint32_t { kModeNormal = 0u, kModeFull = 1u, kModeQuit = 2u };
-
-// LDS: a per-wave ring of two key tiles filled by direct-to-LDS loads during
-// scoring; after scoring the same bytes hold the histogram and then the band
-// entries of the request.
-template <int NQ, int NW, int CHUNK, bool FP8>
-struct IdxSmem {
-  static constexpr int kTileBytes = FP8 ? 32 * 128 : 32 * 256;
-  static constexpr int kSlotBytes = kTileBytes + (FP8 ? 128 : 0);  // FP8: the tile's 32 row scales follow it
-  static constexpr int kRing = NW * 2 * kSlotBytes;
-  static constexpr int kReuse = kBandCap * 8 > kHistBins * 4 ? kBandCap * 8 : kHistBins * 4;
-  static constexpr int kArena = kRing > kReuse ? kRing : kReuse;
-  alignas(16) float w[NQ][64];
-  uint32_t hist[256];                    // radix-select digits
-  uint32_t cbase[kMaxChunksPerSeq + 1];  // band entries before each chunk
-  uint32_t abase[kMaxChunksPerSeq + 1];  // keys >= hi before each chunk
-  uint32_t nabove[kMaxChunksPerSeq];     // keys >= hi per chunk
-  uint32_t bitmap[CHUNK / 32];           // selected positions of one chunk (whole-request writer)
-  uint32_t mm[NQ][NW][2];                // per-wave min / max valid key
-  uint32_t ref[NQ][2];                   // [lo, hi) of this chunk
-  uint32_t sel[4];
-  uint32_t scan[3 * NW];
-  uint32_t flag[4];
-  uint32_t next_tile;
-};
-
-// The LDS object the key DMA writes (the ring) and the ones the streaming
-// loop reads or writes besides it (page ids, keys) are separate variables: the compiler's wait insertion then sees that those reads cannot
-// alias a tile still in flight and does not drain the loads before them.
-template <int NQ, int NW, int CHUNK, bool FP8>
-struct IdxLds {
-  IdxSmem<NQ, NW, CHUNK, FP8>& sm;
-  unsigned char* arena;  // [kArena]: key ring; after scoring the histogram, then the band entries
-  uint32_t* keys;        // [NQ][CHUNK]
-  int* pages;            // [CHUNK / 64]
-};
-
-template <bool FP8>
-struct QOps;
-template <>
-struct QOps<false> {
-  bf16x8 v[8];
-};
-template <>
-struct QOps<true> {
-  i32x8 v[2];
-  int scale[2];
-};
-
-__device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return (uint64_t)v | ((uint64_t)tag << 32); }
-
-// Polls `n` tagged words until each carries `tag` (at most spin_max rounds
-// of sleeping).  Returns false on time-out.
-__device__ __forceinline__ bool poll_tagged(const uint64_t* p, int n, uint32_t tag, int spin_max, uint32_t* vals) {
-  int spins = 0;
-  for (;;) {
-    bool all = true;
-    for (int i = 0; i < n; ++i) {
-      const uint64_t v = xload64(&p[i]);
-      vals[i] = (uint32_t)v;
-      all &= (uint32_t)(v >> 32) == tag;
-    }
-    if (all) return true;
-    if (++spins > spin_max) return false;
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-template <int NQ, int NW, int CHUNK, bool FP8>
-__device__ __forceinline__ void li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ, NW, CHUNK, FP8> lds,
-                                               const uint32_t tag) {
-  IdxSmem<NQ, NW, CHUNK, FP8>& sm = lds.sm;
-  uint32_t* s_keys = lds.keys;  // [NQ][CHUNK]
-
-  constexpr int THREADS = NW * 64;
-  constexpr int NT = CHUNK / 32;  // 32-position tiles per chunk
-  static_assert(NT >= 2 * NW, "each wave starts with two tiles");
-  constexpr int PER = CHUNK / THREADS;  // keys per thread (contiguous positions)
-  static_assert(PER * THREADS == CHUNK && 32 % PER == 0, "chunk splits into whole bit groups per thread");
-  static_assert(kMaxChunksPerSeq <= THREADS, "one thread per chunk of a request");
-
-  // Block -> (request b, chunk c).  The hardware deals blocks to the 8 XCDs
-  // in turn (block id mod 8) and each XCD starts its blocks in id order; the
-  // chunks of a request must be resident together for the exchanges.
-  //  - spread (grids of one round): request b owns blocks b*ncm .. b*ncm+ncm-1
-  //    and chunk c runs as block b*ncm + (c + b) mod ncm, so chunk 0 of
-  //    successive requests rotates over the XCDs;
-  //  - XCD-local (grids of several rounds): request b's chunks all run on XCD
-  //    b mod 8, as blocks 8 ((b / 8) ncm + c) + b mod 8, so a request waits
-  //    only for its own XCD's earlier requests, not for the slowest XCD.
-  const uint32_t ncm_u = (uint32_t)a.n_chunks_max, bid = blockIdx.x;
-  int b, c;
-  if (a.xcd_local) {
-    const uint32_t r = bid >> 3;
-    b = (int)((r / ncm_u) * 8u + (bid & 7u));
-    c = (int)(r % ncm_u);
-  } else {
-    b = (int)(bid / ncm_u);
-    c = (int)((bid % ncm_u + ncm_u - (uint32_t)b % ncm_u) % ncm_u);
-  }
-  if (b >= a.B) return;  // padding of the XCD-local grid (departs in the caller)
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-  const int n = lane & 31, half = lane >> 5;
-  const int t0 = b * NQ;
-  const int s0 = c * CHUNK;
-  const int* bt = a.block_table + (size_t)b * a.max_pages;
-
-  // ---------------------------------------------------------------- prologue (one memory latency)
-  // Page ids (loaded in bounds of the block table whatever the request's
-  // length), the length, q, w and the exchange epoch are all requested at
-  // once; the key tiles follow as soon as the page ids are in LDS.
-  int pg = 0;
-  if (tid < CHUNK / 64 && s0 / 64 + tid < a.max_pages) pg = bt[s0 / 64 + tid];
-  int L = a.seq_lens[b];
-  const float wv = tid < NQ * 64 ? a.w[(size_t)t0 * 64 + tid] : 0.f;
-  QOps<FP8> qa[NQ * 2];  // A operands: the token's 64 heads as two 32-row tiles
-#pragma unroll
-  for (int mt = 0; mt < NQ * 2; ++mt) {
-    const size_t row = (size_t)(t0 + mt / 2) * 64 + 32 * (mt & 1) + n;  // (token, head)
-    if constexpr (!FP8) {
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + row * 128 + 64 * half);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qa[mt].v[j] = qp[j];
-    } else {
-      // The block-scaled 32x32x64 MFMA splits its k range into two blocks of
-      // 32: block 0 is bytes 0..15 of both lane halves, block 1 bytes 16..31,
-      // and block b takes its E8M0 scale from the lanes of half b.  So in
-      // k-step j, bytes 0..15 of this lane carry d = 64j + 16 half + 0..15
-      // (MX group 2j) and bytes 16..31 carry d = 64j + 32 + 16 half + 0..15
-      // (MX group 2j+1); this lane supplies the scale of group 2j + half.
-      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + row * 128;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(qp + 64 * j + 16 * half);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(qp + 64 * j + 32 + 16 * half);
-        qa[mt].v[j] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        qa[mt].scale[j] = a.q_scales[row * 4 + 2 * j + half];
-      }
-    }
-  }
-  uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
-  L = max(0, min(L, a.max_pages * 64));
-  const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
-  if (c >= n_chunks) return;
-  if (tid < CHUNK / 64) lds.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
-  if (tid < NQ * 64) sm.w[tid / 64][tid % 64] = wv;
-  const int n_valid = min(CHUNK, L - s0);     // positions of this chunk in the cache (>= 1)
-  const int nt_used = (n_valid + 31) / 32;    // tiles that hold any of them
-  if (tid == 0) sm.next_tile = 2 * NW;
-  // tiles nobody scores hold no visible position: their keys are 0
-  for (int i = nt_used * 32 + tid; i < CHUNK; i += THREADS)
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) s_keys[j * CHUNK + i] = 0u;
-  __syncthreads();
-
-  // ---------------------------------------------------------------- score
-  // Tiles of 32 positions (inside one page) are dealt to the waves on demand
-  // (an LDS counter), so the chunk's waves finish together.  Each wave moves
-  // its tiles by direct-to-LDS loads into a private two-slot ring; each DMA
-  // instruction reads one contiguous kilobyte of the tile (eight lanes per
-  // 128-byte line) and writes lane l's 16 bytes to slot 64i + l; inside a
-  // line the 16-byte chunks are XOR-swizzled by (row & 7), so the MFMA
-  // operand reads (row n, fixed column) hit distinct banks.  FP8 tiles bring
-  // their 32 row scales along (one more direct-to-LDS load, 4 bytes a lane).
-  constexpr int TB = IdxSmem<NQ, NW, CHUNK, FP8>::kTileBytes;
-  constexpr int SB = IdxSmem<NQ, NW, CHUNK, FP8>::kSlotBytes;
-  constexpr int DMA_PER_TILE = TB / 1024 + (FP8 ? 1 : 0);
-  constexpr int ROW = FP8 ? 128 : 256;  // bytes per key row
-  constexpr int RPI = 1024 / ROW;       // rows per DMA instruction
-  unsigned char* ring = lds.arena + wid * 2 * SB;
-  // this lane's share of every DMA instruction: row (within the instruction)
-  // and the 16-byte chunk of that row
-  const int dma_row = lane / (64 / RPI);
-  const int dma_line = FP8 ? 0 : (lane >> 3) & 1;
-  auto issue = [&](int tile, int slot_i) {
-    const int lp = tile * 32;  // position inside the chunk
-    const size_t row0 = (size_t)lds.pages[lp >> 6] * 64 + (lp & 32);
-    const char* base = static_cast<const char*>(a.k) + row0 * ROW;
-    unsigned char* dst = ring + slot_i * SB;
-#pragma unroll
-    for (int i = 0; i < TB / 1024; ++i) {
-      const int row = RPI * i + dma_row;
-      const int col = 8 * dma_line + ((lane & 7) ^ (row & 7));
-      __builtin_amdgcn_global_load_lds(base + row * ROW + 16 * col, (lds_void*)(dst + 1024 * i), 16, 0, 0);
-    }
-    if constexpr (FP8) {
-      if (lane < 32)
-        __builtin_amdgcn_global_load_lds(static_cast<const uint32_t*>(a.k_scales) + row0 + lane, (lds_void*)(dst + TB),
-                                         4, 0, 0);
-    }
-  };
-  // `issued` counts this wave's vector-memory instructions; mark[s] is the
-  // count just after slot s's tile was issued.
-  uint32_t issued = 0, mark[2] = {0u, 0u};
-  auto issue_counted = [&](int tile, int slot_i) {
-    issue(tile, slot_i);
-    issued += DMA_PER_TILE;
-    mark[slot_i] = issued;
-  };
-  // The tile counter is bumped by an LDS atomic written as the instruction
-  // itself (with its own wait): as a compiler atomic it would make the wait
-  // pass drain every direct-to-LDS load in flight first.
-  const uint32_t next_addr = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)&sm.next_tile;
-  auto grab = [&]() -> int {
-    uint32_t t = 0;
-    if (lane == 0)  // one lane: one tile
-      asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(t) : "v"(next_addr), "v"(1u) : "memory");
-    return (int)min(__builtin_amdgcn_readfirstlane(t), (uint32_t)nt_used);
-  };
-  // the first two tiles of every wave; the one after them is dealt now
-  int cur = wid, nxt = wid + NW, pre = nt_used;
-  if (cur < nt_used) issue_counted(cur, 0);
-  if (nxt < nt_used) issue_counted(nxt, 1);
-
-  int vis[NQ];
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) vis[j] = max(0, L - NQ + j + 1);
-  uint32_t kmin[NQ], kmax[NQ];  // this lane's smallest / largest valid key
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    kmin[j] = 0xffffffffu;
-    kmax[j] = 0u;
-  }
-
-  // LDS byte offset of (row, 16-byte chunk) inside a tile
-  auto slot = [&](int row, int col) {
-    return 1024 * (row / RPI) + 16 * ((64 / RPI) * (row % RPI) + 8 * (col >> 3) + ((col & 7) ^ (row & 7)));
-  };
-
-  auto compute = [&](int tile, int slot_i) {
-    const int pos0 = s0 + tile * 32;
-    const unsigned char* src = ring + slot_i * SB;
-    f32x16 acc[NQ * 2];
-#pragma unroll
-    for (int mt = 0; mt < NQ * 2; ++mt) acc[mt] = (f32x16){};
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // k-step j: row n, bytes 128 half + 16 j = chunk 8 half + j
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(src + slot(n, 8 * half + j));
-#pragma unroll
-        for (int mt = 0; mt < NQ * 2; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt].v[j], kb, acc[mt], 0, 0, 0);
-      }
-    }
-    // FP8 row n's scale word: its f32 scale, or (MXFP8 keys) its four E8M0
-    // codes, group g in byte g
-    const uint32_t ksw = FP8 ? reinterpret_cast<const uint32_t*>(src + TB)[n] : 0u;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // k-step j: row n, bytes 64 j + 16 half (chunk 4j + half) and 64 j + 32 + 16 half
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(src + slot(n, 4 * j + half));
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(src + slot(n, 4 * j + 2 + half));
-        const i32x8 kb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        // this lane supplies the B scale of MX group 2j + half of row n (the
-        // same lane-half rule as the query's A scales); 127 = 1 for row scales
-        const int kbs = a.k_mx ? (int)((ksw >> (8 * (2 * j + half))) & 0xffu) : 127;
-#pragma unroll
-        for (int mt = 0; mt < NQ * 2; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt].v[j], kb, acc[mt], 0, 0, 0,
-                                                                   qa[mt].scale[j], 0, kbs);
-      }
-    }
-    const float kscale = (FP8 && !a.k_mx) ? __uint_as_float(ksw) : 1.f;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      float part = 0.f;
-#pragma unroll
-      for (int mh = 0; mh < 2; ++mh) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // output rows 8g+4*half+0..3 of this 32-head tile: four consecutive heads
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(&sm.w[j][32 * mh + 8 * g + 4 * half]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part += w4[i] * fmaxf(acc[2 * j + mh][4 * g + i], 0.f);
-        }
-      }
-      part += __shfl_xor(part, 32, kWave);
-      if constexpr (FP8) part *= kscale;  // positive per-row scale commutes with ReLU (1 for MXFP8 keys)
-      if (half == 0) {
-        const int s = pos0 + n;
-        const uint32_t key = (s < vis[j]) ? score_key(part) : 0u;
-        s_keys[j * CHUNK + tile * 32 + n] = key;
-        if (key != 0u) {
-          kmin[j] = min(kmin[j], key);
-          kmax[j] = max(kmax[j], key);
-        }
-      }
-    }
-  };
-
-  if (nxt < nt_used) pre = grab();
-  int slot_i = 0;
-#pragma unroll 1
-  while (cur < nt_used) {
-    // the current tile has landed once at most the instructions issued after
-    // its DMA are outstanding (wave-uniform count: 0 or one tile's DMA)
-    switch (min(issued - mark[slot_i], 2u * DMA_PER_TILE + 2u)) {
-#define SLI_WAIT_CASE(N) case N: SLI_WAIT_VMCNT(N); break;
-      SLI_WAIT_CASE(0) SLI_WAIT_CASE(1) SLI_WAIT_CASE(2) SLI_WAIT_CASE(3) SLI_WAIT_CASE(4) SLI_WAIT_CASE(5)
-      SLI_WAIT_CASE(6) SLI_WAIT_CASE(7) SLI_WAIT_CASE(8) SLI_WAIT_CASE(9) SLI_WAIT_CASE(10) SLI_WAIT_CASE(11)
-      SLI_WAIT_CASE(12) SLI_WAIT_CASE(13) SLI_WAIT_CASE(14) SLI_WAIT_CASE(15) SLI_WAIT_CASE(16) SLI_WAIT_CASE(17)
-      SLI_WAIT_CASE(18)
-#undef SLI_WAIT_CASE
-      default: SLI_WAIT_VMCNT(0); break;
-    }
-    compute(cur, slot_i);
-    int g = nt_used;
-    if (pre < nt_used) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this slot's operand reads are done
-      issue_counted(pre, slot_i);
-      g = grab();
-    }
-    cur = nxt;
-    nxt = pre;
-    pre = g;
-    slot_i ^= 1;
-  }
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    const uint32_t mn = wave_min(kmin[j]), mx = wave_max(kmax[j]);
-    if (lane == 0) {
-      sm.mm[j][wid][0] = mn;
-      sm.mm[j][wid][1] = mx;
-    }
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- selection
-  const int K = a.top_k;
-  const size_t ncm = (size_t)a.n_chunks_max;
-  bool any_sel = false;
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) any_sel |= vis[j] > K;
-  // Tokens that see at most K positions keep them all: chunk c's positions go
-  // to out[s0 ...] (every earlier chunk is full); the chunk holding the last
-  // visible position pads the row with -1.
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    if (vis[j] > K) continue;
-    int32_t* out = a.idx_out + (size_t)(t0 + j) * K;
-    for (int i = tid; i < CHUNK; i += THREADS)
-      if (s0 + i < vis[j]) out[s0 + i] = s0 + i;
-    if (c == (vis[j] == 0 ? 0 : (vis[j] - 1) / CHUNK))
-      for (int i = vis[j] + tid; i < K; i += THREADS) out[i] = -1;
-  }
-  if (!any_sel) return;  // (every workgroup of the request decides alike: no exchange)
-
-  // 1. the interval [lo_c, hi_c) holding this chunk's R-th largest key, R its quota
-  uint32_t* hist = reinterpret_cast<uint32_t*>(lds.arena);  // [kHistBins] (the key ring is free now)
-#pragma unroll 1
-  for (int j = 0; j < NQ; ++j) {
-    if (vis[j] <= K) continue;
-    const int valid = max(0, min(CHUNK, vis[j] - s0));
-    const int nv = (vis[j] + CHUNK - 1) / CHUNK;   // chunks holding visible positions (>= 1)
-    const int v_last = vis[j] - (nv - 1) * CHUNK;  // visible positions of the last of them
-    int R = (K + nv - 1) / nv;
-    if (nv > 1 && v_last < CHUNK) {
-      const int r_tail = (int)((long long)K * v_last / vis[j]);  // <= v_last (K < vis)
-      R = c == nv - 1 ? r_tail : (K - r_tail + nv - 2) / (nv - 1);
-    }
-    uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mn = min(mn, sm.mm[j][w][0]);
-      mx = max(mx, sm.mm[j][w][1]);
-    }
-    if (valid == 0) {
-      // no visible position: an empty interval, neutral for min lo and max hi
-      if (tid == 0) sm.ref[j][0] = 0xffffffffu, sm.ref[j][1] = 0u;
-    } else if (R == 0) {
-      // no quota: nothing counted at or above lo_c, and no key at or above hi_c
-      if (tid == 0) sm.ref[j][0] = 0xffffffffu, sm.ref[j][1] = min(mx, 0xfffffffeu) + 1u;
-    } else if (mn == mx) {
-      if (tid == 0) sm.ref[j][0] = mn, sm.ref[j][1] = mn + 1u;
-    } else {
-      const int top = 31 - __clz(mn ^ mx);
-      const int shift = max(0, top - 11);
-      const uint32_t base = mn >> shift;  // bin of a key: (key >> shift) - base, < 4096
-      for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const uint32_t key = s_keys[j * CHUNK + tid * PER + i];
-        if (key != 0u) atomicAdd(&hist[(key >> shift) - base], 1u);
-      }
-      __syncthreads();
-      // thread t owns bins kHistBins-1 - BPT t - r, r < BPT (descending keys)
-      constexpr int BPT = kHistBins / THREADS;
-      uint32_t h[BPT], sum = 0;
-#pragma unroll
-      for (int r = 0; r < BPT; ++r) {
-        h[r] = hist[kHistBins - 1 - BPT * tid - r];
-        sum += h[r];
-      }
-      uint32_t tot;
-      const uint32_t before = block_excl_scan(sum, sm.scan, tot);
-      if (before < (uint32_t)R && (uint32_t)R <= before + sum) {
-        uint32_t acc = before;
-#pragma unroll
-        for (int r = 0; r < BPT; ++r) {
-          if (acc < (uint32_t)R && (uint32_t)R <= acc + h[r]) {
-            const uint32_t bin = (uint32_t)(kHistBins - 1 - BPT * tid - r) + base;
-            const uint64_t up = (uint64_t)(bin + 1u) << shift;
-            sm.ref[j][0] = bin << shift;
-            sm.ref[j][1] = up > 0xffffffffull ? 0xffffffffu : (uint32_t)up;
-          }
-          acc += h[r];
-        }
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint64_t* rp = a.refs + ((size_t)(t0 + j) * ncm + c) * 2;
-      xstore64(&rp[0], tagged(sm.ref[j][0], tag));
-      xstore64(&rp[1], tagged(sm.ref[j][1], tag));
-    }
-  }
-
-  // exchange 1: every chunk's [lo_c, hi_c) -> the request's [lo, hi)
-  uint32_t lo_ref[NQ], hi_ref[NQ];
-  {
-    uint32_t l[NQ], h[NQ];
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      l[j] = 0xffffffffu;
-      h[j] = 0u;
-      if (vis[j] > K && tid < n_chunks) {
-        uint32_t v[2];
-        ok &= poll_tagged(a.refs + ((size_t)(t0 + j) * ncm + tid) * 2, 2, tag, a.spin_max, v);
-        l[j] = v[0];
-        h[j] = v[1];
-      }
-    }
-    const bool refs_ok = __syncthreads_and(ok) != 0;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      l[j] = wave_min(l[j]);
-      h[j] = wave_max(h[j]);
-      if (lane == 0) {
-        sm.mm[j][wid][0] = l[j];
-        sm.mm[j][wid][1] = h[j];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      uint32_t lm = 0xffffffffu, hm = 0u;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        lm = min(lm, sm.mm[j][w][0]);
-        hm = max(hm, sm.mm[j][w][1]);
-      }
-      // a workgroup that did not see every chunk's interval in time treats
-      // all of its keys as band, which keeps the selection exact
-      lo_ref[j] = refs_ok ? max(lm, 1u) : 1u;
-      hi_ref[j] = refs_ok ? hm : 0xffffffffu;
-    }
-  }
-
-  // 2. publish keys >= hi (back of the region) and the band [lo, hi) (front),
-  //    both in position order, then the tagged counts
-#pragma unroll 1
-  for (int j = 0; j < NQ; ++j) {
-    if (vis[j] <= K) continue;
-    uint32_t kk[PER];
-    uint32_t na = 0, nb = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      kk[i] = s_keys[j * CHUNK + tid * PER + i];
-      na += kk[i] >= hi_ref[j] ? 1u : 0u;
-      nb += (kk[i] >= lo_ref[j] && kk[i] < hi_ref[j]) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t off = block_excl_scan(na | (nb << 16), sm.scan, tot);  // both counts <= CHUNK < 2^16
-    uint32_t oa = off & 0xffffu, ob = off >> 16;
-    uint64_t* reg = a.cand + ((size_t)(t0 + j) * ncm + c) * CHUNK;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint64_t e = (uint64_t)kk[i] | ((uint64_t)(uint32_t)(s0 + tid * PER + i) << 32);
-      if (kk[i] >= hi_ref[j]) {
-        xstore64(&reg[CHUNK - 1 - oa], e);
-        ++oa;
-      } else if (kk[i] >= lo_ref[j]) {
-        xstore64(&reg[ob], e);
-        ++ob;
-      }
-    }
-    if (tid == 0) sm.flag[2 + (j & 1)] = tot;
-  }
-  // the lists are complete in memory before the counts that announce them
-  wait_vmem();
-  __syncthreads();
-  uint32_t old2 = 0;
-  if (tid == 0) {
-#pragma unroll
-    for (int j = 0; j < NQ; ++j)
-      if (vis[j] > K) xstore64(&a.cnts[(size_t)(t0 + j) * ncm + c], tagged(sm.flag[2 + (j & 1)], tag));
-    old2 = __hip_atomic_fetch_add(&ctr[kArrive2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // exchange 2: every chunk's counts
-  uint32_t cnt_v[NQ];
-  {
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      cnt_v[j] = 0u;
-      if (vis[j] > K && tid < n_chunks) ok &= poll_tagged(&a.cnts[(size_t)(t0 + j) * ncm + tid], 1, tag, a.spin_max, &cnt_v[j]);
-    }
-    const bool all_ok = __syncthreads_and(ok) != 0;
-    if (tid == 0) {
-      uint32_t mode = kModeNormal;
-      const bool last = old2 == (uint32_t)n_chunks - 1;
-      if (last) {
-        // last to arrive: writes the whole request if some workgroup gave up
-        const uint32_t st = __hip_atomic_fetch_or(&ctr[kState], kStLast, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (st & kStGaveUp) mode = kModeFull;
-      } else if (!all_ok) {
-        const uint32_t st = __hip_atomic_fetch_or(&ctr[kState], kStGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!(st & kStLast)) mode = kModeQuit;  // the last one has not arrived: it will write this share
-      }
-      sm.flag[1] = mode;
-      sm.flag[0] = all_ok ? 1u : 0u;
-      // done with the request's exchange state: the last to get here resets it
-      const uint32_t d = __hip_atomic_fetch_add(&ctr[kDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (d == (uint32_t)n_chunks - 1) {
-        __hip_atomic_store(&ctr[kArrive2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctr[kState], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctr[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-  }
-  const uint32_t mode = sm.flag[1];
-  if (mode == kModeQuit) return;
-  if (sm.flag[0] == 0u) {
-    // the last one has arrived, so every count is in memory: read them again
-#pragma unroll
-    for (int j = 0; j < NQ; ++j)
-      if (vis[j] > K && tid < n_chunks)
-        poll_tagged(&a.cnts[(size_t)(t0 + j) * ncm + tid], 1, tag, 1 << 30, &cnt_v[j]);
-    __syncthreads();
-  }
-
-  // 3. exact select among the band entries, then the writes
-  uint32_t* s_bk = reinterpret_cast<uint32_t*>(lds.arena);       // [kBandCap] band keys
-  int32_t* s_bp = reinterpret_cast<int32_t*>(s_bk + kBandCap);  // [kBandCap] their positions
-#pragma unroll 1
-  for (int j = 0; j < NQ; ++j) {
-    if (vis[j] <= K) continue;
-    const size_t tok = (size_t)(t0 + j);
-    // A chunk's two counts fit 16 bits each (<= CHUNK), but the request's
-    // band can hold every position of the request (scores that rise with
-    // position put each chunk's bracket at a different key): the prefixes over
-    // the chunks are taken as separate 32-bit scans.
-    const uint32_t cv[2] = {cnt_v[j] & 0xffffu, cnt_v[j] >> 16};  // keys >= hi, band keys (0 past n_chunks)
-    uint32_t cpre[2], ctot[2];
-    block_excl_scan_n<2>(cv, sm.scan, cpre, ctot);
-    if (tid < n_chunks) {
-      sm.abase[tid] = cpre[0];
-      sm.cbase[tid] = cpre[1];
-      sm.nabove[tid] = cv[0];
-    }
-    if (tid == 0) {
-      sm.abase[n_chunks] = ctot[0];
-      sm.cbase[n_chunks] = ctot[1];
-    }
-    __syncthreads();
-    const uint32_t A = ctot[0], NB = ctot[1];
-    const int need = K - (int)A;  // >= 1: fewer than K keys reach hi
-    const bool in_lds = NB <= (uint32_t)kBandCap;
-    auto gaddr = [&](int i, uint32_t sl) { return (tok * ncm + i) * CHUNK + sl; };
-    // flat band entry f -> chunk (binary search over the prefix offsets)
-    auto chunk_of = [&](int f) {
-      int lo = 0, hi = n_chunks;  // cbase[lo] <= f < cbase[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int)sm.cbase[mid] <= f) lo = mid; else hi = mid;
-      }
-      return lo;
-    };
-    if (in_lds) {
-      // up to eight loads per thread in flight at once (one memory latency
-      // per 8 x blockDim entries)
-      constexpr int LPT = kBandCap / THREADS < 8 ? kBandCap / THREADS : 8;
-#pragma unroll 1
-      for (int f0 = 0; f0 < (int)NB; f0 += LPT * THREADS) {
-        uint64_t ev[LPT];
-#pragma unroll
-        for (int r = 0; r < LPT; ++r) {
-          const int f = f0 + tid + r * THREADS;
-          ev[r] = 0ull;
-          if (f < (int)NB) {
-            const int i = chunk_of(f);
-            ev[r] = xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < LPT; ++r) {
-          const int f = f0 + tid + r * THREADS;
-          if (f < (int)NB) {
-            s_bk[f] = (uint32_t)ev[r];
-            s_bp[f] = (int32_t)(ev[r] >> 32);
-          }
-        }
-      }
-      __syncthreads();
-    }
-    auto key_at = [&](int f) -> uint32_t {
-      if (in_lds) return s_bk[f];
-      const int i = chunk_of(f);
-      return (uint32_t)xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
-    };
-    int ngt;
-    uint32_t tau;
-    if (in_lds && NB <= 8u * kWave) {
-      // the usual band (a few hundred entries): one wave selects, no block barriers
-      if (wid == 0) {
-        int g;
-        const uint32_t tv = wave_radix_select<8>([&](int f) { return s_bk[f]; }, (int)NB, need, sm.hist, g);
-        if (lane == 0) {
-          sm.sel[2] = tv;
-          sm.sel[3] = (uint32_t)g;
-        }
-      }
-      __syncthreads();
-      tau = sm.sel[2];
-      ngt = (int)sm.sel[3];
-    } else {
-      tau = in_lds ? block_radix_select<kBandCap / THREADS>(key_at, (int)NB, need, sm.hist, sm.sel, ngt)
-                   : block_radix_select_big(key_at, (int)NB, need, sm.hist, sm.sel, ngt);
-    }
-    const uint32_t ties = (uint32_t)(need - ngt);  // keys equal to tau that are taken, lowest positions first
-    int32_t* out = a.idx_out + tok * K;
-
-    if (mode == kModeNormal) {
-      // band entries before this chunk: how many are > tau, how many tie
-      // (from global memory: eight reads per thread in flight)
-      uint32_t gt = 0, eq = 0;
-      const int cb = (int)sm.cbase[c];
-      constexpr int LPT = 8;
-#pragma unroll 1
-      for (int f0 = tid; f0 < cb; f0 += LPT * THREADS) {
-        uint32_t kv[LPT];
-#pragma unroll
-        for (int r = 0; r < LPT; ++r) kv[r] = f0 + r * THREADS < cb ? key_at(f0 + r * THREADS) : 0u;
-#pragma unroll
-        for (int r = 0; r < LPT; ++r) {
-          const bool in = f0 + r * THREADS < cb;
-          gt += (in && kv[r] > tau) ? 1u : 0u;
-          eq += (in && kv[r] == tau) ? 1u : 0u;
-        }
-      }
-      // own keys in position order: selected for certain (>= hi, or in the
-      // band and > tau) or tied at tau
-      uint32_t kk[PER], nd = 0, nt = 0;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        kk[i] = s_keys[j * CHUNK + tid * PER + i];
-        const bool band = kk[i] >= lo_ref[j] && kk[i] < hi_ref[j];
-        nd += (kk[i] >= hi_ref[j] || (band && kk[i] > tau)) ? 1u : 0u;
-        nt += (band && kk[i] == tau) ? 1u : 0u;
-      }
-      // one scan: totals of the earlier chunks' band (32 bits each: the band
-      // may hold most of the request), prefixes of this chunk's keys (packed:
-      // both <= CHUNK < 2^16)
-      const uint32_t sv[3] = {gt, eq, nd | (nt << 16)};
-      uint32_t spre[3], stot[3];
-      block_excl_scan_n<3>(sv, sm.scan, spre, stot);
-      const uint32_t gt_before = stot[0], eq_before = stot[1], pre = spre[2];
-      const uint32_t avail = ties > eq_before ? ties - eq_before : 0u;  // ties left for this chunk
-      uint32_t tr = pre >> 16;                                            // ties of this chunk before my keys
-      uint32_t o = sm.abase[c] + gt_before + min(ties, eq_before) + (pre & 0xffffu) + min(avail, tr);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const bool band = kk[i] >= lo_ref[j] && kk[i] < hi_ref[j];
-        const bool tie = band && kk[i] == tau;
-        if (kk[i] >= hi_ref[j] || (band && kk[i] > tau) || (tie && tr < avail)) out[o++] = s0 + tid * PER + i;
-        tr += tie ? 1u : 0u;
-      }
-    } else {
-      // kModeFull: the whole request, chunk by chunk, from the published
-      // lists (keys >= hi all taken; band entries by tau and tie rank)
-      uint32_t off = 0, eq_seen = 0;
-#pragma unroll 1
-      for (int i = 0; i < n_chunks; ++i) {
-        for (int wd = tid; wd < CHUNK / 32; wd += THREADS) sm.bitmap[wd] = 0u;
-        __syncthreads();
-        const int ci0 = i * CHUNK;
-        for (uint32_t e = tid; e < sm.nabove[i]; e += THREADS) {
-          const int pos = (int)(xload64(&a.cand[gaddr(i, CHUNK - 1 - e)]) >> 32);
-          atomicOr(&sm.bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
-        }
-        const int f0 = (int)sm.cbase[i], f1 = (int)sm.cbase[i + 1];
-#pragma unroll 1
-        for (int fb = f0; fb < f1; fb += THREADS) {
-          const int f = fb + tid;
-          uint64_t ev = 0ull;
-          if (f < f1)
-            ev = in_lds ? ((uint64_t)s_bk[f] | ((uint64_t)(uint32_t)s_bp[f] << 32)) : xload64(&a.cand[gaddr(i, f - f0)]);
-          const uint32_t key = (uint32_t)ev;
-          const bool tie = f < f1 && key == tau;
-          uint32_t et;
-          const uint32_t rank = eq_seen + block_excl_scan(tie ? 1u : 0u, sm.scan, et);
-          if (f < f1 && (key > tau || (tie && rank < ties))) {
-            const int pos = (int)(ev >> 32);
-            atomicOr(&sm.bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
-          }
-          eq_seen += et;
-        }
-        __syncthreads();
-        // emit in position order: thread t owns bits PER*t .. PER*t + PER-1
-        const uint32_t word = sm.bitmap[(PER * tid) >> 5];
-        const uint32_t bits = (word >> ((PER * tid) & 31)) & ((1u << PER) - 1u);
-        uint32_t et;
-        uint32_t o = off + block_excl_scan((uint32_t)__popc(bits), sm.scan, et);
-#pragma unroll
-        for (int r = 0; r < PER; ++r)
-          if ((bits >> r) & 1u) out[o++] = ci0 + PER * tid + r;
-        off += et;
-        __syncthreads();
-      }
-    }
-    __syncthreads();  // LDS band arrays and offsets are reused by the next token
-  }
-}
-
-template <int NQ, int NW, int CHUNK, bool FP8>
+template <int NQ, int NW, int CHUNK, bool FP8, int RS>
 __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs a) {
-  __shared__ IdxSmem<NQ, NW, CHUNK, FP8> sm;
-  __shared__ __attribute__((aligned(16))) unsigned char arena[IdxSmem<NQ, NW, CHUNK, FP8>::kArena];
+  __shared__ IdxSmem<NQ, NW, CHUNK, FP8, RS> sm;
+  __shared__ __attribute__((aligned(16))) unsigned char arena[IdxSmem<NQ, NW, CHUNK, FP8, RS>::kArena];
   __shared__ uint32_t keys[NQ * CHUNK];
   __shared__ int pages[CHUNK / 64];
   uint32_t* grid_line = a.counters + (size_t)kMaxSeqs * kCounterStride;
   const uint32_t tag = __builtin_amdgcn_readfirstlane(xload(&grid_line[kGridEpoch]) + 1u);
-  li_decode_body<NQ, NW, CHUNK, FP8>(a, IdxLds<NQ, NW, CHUNK, FP8>{sm, arena, keys, pages}, tag);
+  int b;
+  (void)li_decode_body<NQ, NW, CHUNK, FP8, RS>(a, IdxLds<NQ, NW, CHUNK, FP8, RS>{sm, arena, keys, pages}, tag, b);
   // every workgroup (those without work included) departs once; the last
   // resets the count and advances the epoch for the next call
   if (threadIdx.x == 0) {
@@ -815,11 +27,11 @@ __global__ __launch_bounds__(NW * 64) void li_decode_kernel(const IdxDecodeArgs 
   }
 }
 
-template <int NQ, int NW, int CHUNK, bool FP8>
+template <int NQ, int NW, int CHUNK, bool FP8, int RS = 2>
 static hipError_t launch_one(const IdxDecodeArgs& a, hipStream_t stream) {
   const long long blocks = a.xcd_local ? (long long)((a.B + 7) / 8) * 8 * a.n_chunks_max : (long long)a.B * a.n_chunks_max;
   dim3 grid((unsigned)blocks);
-  hipLaunchKernelGGL((li_decode_kernel<NQ, NW, CHUNK, FP8>), grid, dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((li_decode_kernel<NQ, NW, CHUNK, FP8, RS>), grid, dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -855,6 +67,9 @@ hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStr
     // streams while the other selects (eight-wave ones fill a CU alone)
     if (fp8 && a.xcd_local)
       return a.n_q == 1 ? launch_one<1, 4, 4096, true>(a, stream) : launch_one<2, 4, 4096, true>(a, stream);
+#ifdef SLI_PROBE_W4R4
+    if (a.n_q == 1 && !fp8) return launch_one<1, 4, 4096, false, 4>(a, stream);
+#endif
     if (a.n_q == 1) return fp8 ? launch_one<1, 8, 4096, true>(a, stream) : launch_one<1, 8, 4096, false>(a, stream);
     if (a.n_q == 2 && fp8) return launch_one<2, 8, 4096, true>(a, stream);
   }

@@ -62,6 +62,14 @@ struct SfaArgs {
   float* part_ml;  // [T][n_splits][H][2]   (running max in log2 units, sum)
 };
 
+// The single-launch decode step: the indexer's arguments and workspace
+// (n_q = 1, bf16, 4096-position chunks, one workgroup per chunk) and the
+// attention's (T = B, 128 heads, split partials in the workspace).
+struct StepArgs {
+  IdxDecodeArgs idx;
+  SfaArgs att;
+};
+
 struct QuantArgs {
   int n_rows, row_len;  // row_len % 32 == 0
   const void* x;        // bf16 [n_rows][row_len]
@@ -98,6 +106,7 @@ hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStr
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_decode_step(const StepArgs& s, hipStream_t stream);
 int sfa_heads_per_block(int H, bool fp8);
 
 }  // namespace sli

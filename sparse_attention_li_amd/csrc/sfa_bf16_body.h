@@ -1,0 +1,720 @@
+// Sparse MLA attention over bf16 latent rows, every head (up to 128) of a
+// token in one four-wave workgroup: the device body shared by the attention
+// launch (sfa.hip) and the single-launch decode step (decode_step.hip).
+// What it computes and the split merge are described in sfa.hip.
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace sli {
+
+constexpr int kTileRows = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// LDS tile layout.  A tile holds 32 rows x 72 chunks of 16 bytes (one chunk =
+// 8 bf16), 36 KiB, filled by 36 wave-wide direct-to-LDS loads.  Load i copies
+// one 128-byte line (chunks 8g..8g+7, g = i/4) of the eight rows 8(i%4)..+7:
+// eight lanes per row, so every load reads whole cache lines.  Lane l of load
+// i lands at byte 16(64i + l); inside its row the chunk is placed at
+// position (chunk & 7) ^ f(row), a swizzle under which both operand reads are
+// conflict-free: the logit operand read (eight rows, one chunk) and the
+// transposed read (four consecutive rows, two adjacent chunks).
+constexpr int kTileBytes = 36 * 1024;
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return 16 * (64 * (4 * (chunk >> 3) + (row >> 3)) + 8 * (row & 7) + ((chunk & 7) ^ swz(row)));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 latent rows, every head of the token in one workgroup.
+//
+// Wave w computes the full 576-wide logits and the online softmax of heads
+// 32w .. 32w+31 (its q^T operands, 144 VGPRs, stay resident), and the output
+// of all the heads for latent columns 128w .. 128w+127 (16 accumulator tiles):
+// a wave reads a quarter of each tile transposed, instead of all of it, and
+// the softmax weights of every head reach every wave through an 8 KiB LDS
+// buffer, laid out as the output MFMA's operand registers.  Each selected row
+// crosses the memory system once per slice.  Tiles move through a four-slot
+// LDS ring: two tiles are in flight while two are consumed (the logits of one,
+// the output product of the one before).
+// Read schedule of the bf16 kernel's output product (32 MFMAs per tile and
+// wave; MFMA j uses k-block kk = j / 16, column tile mm = (j / 4) % 4 and head
+// block hb = j % 4, i.e. transposed pair pi = 4 kk + mm and weights
+// P(kk, hb)).  LDS reads in issue order: P(0, 0..3), pairs 0 .. A-1; pair
+// pi + A just before the first MFMA of pair pi; P(1, hb) just after the last
+// MFMA that uses P(0, hb).  LDS reads of one wave complete in order, so MFMA
+// j waits until no more than issued - needed of them are outstanding.
+// reads issued before MFMA j's wait (its own pair issue included)
+__host__ __device__ constexpr int sfa_pv_issued(int ahead, int j) {
+  int cnt = 4 + 2 * ahead;
+  for (int i = 0; i <= j; ++i) {
+    const int kk = i >> 4, mm = (i >> 2) & 3, pi = 4 * kk + mm;
+    if ((i & 3) == 0 && pi + ahead < 8) cnt += 2;
+    if (i < j && kk == 0 && mm == 3) cnt += 1;
+  }
+  return cnt;
+}
+// one past the issue index of the last read MFMA j needs
+__host__ __device__ constexpr int sfa_pv_needed(int ahead, int j) {
+  const int kk = j >> 4, mm = (j >> 2) & 3, hb = j & 3, pi = 4 * kk + mm;
+  const int p_at = kk == 0 ? hb : sfa_pv_issued(ahead, 12 + hb);
+  const int pair_last = pi < ahead ? 5 + 2 * pi : sfa_pv_issued(ahead, 4 * (pi - ahead)) - 1;
+  return (p_at > pair_last ? p_at : pair_last) + 1;
+}
+__host__ __device__ constexpr int sfa_pv_outstanding(int ahead, int j) {
+  return sfa_pv_issued(ahead, j) - sfa_pv_needed(ahead, j);
+}
+__host__ __device__ constexpr bool sfa_pv_schedule_ok(int ahead) {
+  for (int j = 0; j < 32; ++j) {
+    const int w = sfa_pv_outstanding(ahead, j);
+    if (w < 0 || w > 8) return false;
+  }
+  return sfa_pv_outstanding(ahead, 31) == 0;  // everything awaited by the last MFMA
+}
+constexpr int kPvAhead = 1;  // transposed pairs read ahead of their first MFMA
+static_assert(sfa_pv_schedule_ok(1) && sfa_pv_schedule_ok(2), "output-product read schedule");
+
+#ifndef SLI_NO_PINS
+#define SLI_PIN_V(x) asm volatile("" : "+v"(x))
+#define SLI_PIN_A(x) asm volatile("" : "+a"(x))
+#else
+#define SLI_PIN_V(x)
+#define SLI_PIN_A(x)
+#endif
+// LDS of the all-heads body: four ring slots of one tile each (the targets
+// of the direct-to-LDS gathers; no C++ access may touch a slot while loads
+// into any slot are in flight), the weights buffer and the slice's row ids.
+struct SfaBf16Lds {
+  char* slot0;
+  char* slot1;
+  char* slot2;
+  char* slot3;
+  char* pbuf;  // 4 * 2 * 64 * 16 bytes
+  int* rows;   // ROWS entries
+};
+
+// Token t, index-row slice `split` (ROWS >= the slice's rows rounded up to
+// whole tiles).  FUSED (the single-launch step): the caller has written the
+// pool rows to attend, own_cnt of them (all valid), into lds.rows; with
+// `direct` the result is the token's output, else the partial of slot
+// `split`, written through to memory for the workgroup that merges it.
+template <int NW, int ROWS, bool FUSED>
+__device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds& lds, const int t, const int split,
+                                              const int own_cnt = 0, const bool direct = false) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = 36;        // 16-wide k-steps of the 576-wide logits
+  constexpr int MI = 16;        // 32-column output tiles
+  constexpr int PVS = 2 * MI;   // output MFMAs per tile
+  constexpr int DPW = 36 / NW;  // direct-to-LDS loads per wave per tile
+  constexpr int PDL = 4;        // logit operand reads issued this many steps ahead
+  static_assert(36 % NW == 0, "the 36 loads of a tile are dealt evenly over the waves");
+  static_assert(2 * DPW <= 63, "two tiles of loads in flight per wave");
+  static_assert(3 * DPW <= PVS, "a wave's loads of a tile fit between the output MFMAs");
+  static_assert(PDL <= 4, "explicit LDS-read waits cover at most 4 steps in flight");
+  static_assert(NW == 4, "four head blocks and four column quarters");
+  static_assert(ROWS % NT == 0, "row ids resolved in whole passes");
+  char* const slot0 = lds.slot0;
+  char* const slot1 = lds.slot1;
+  char* const slot2 = lds.slot2;
+  char* const slot3 = lds.slot3;
+  char* const pbuf = lds.pbuf;
+  int* const rows = lds.rows;
+  // The last 4 KiB of a slot hold the tile's rope columns, read only by the
+  // logits; once every wave is past them they carry the tile's softmax
+  // rescale factors (128 floats at +0, one flag per head block at +512).  The
+  // prologue's minimum row sits there in slot 3 (no tile has been loaded yet).
+  constexpr int kRope = 32768;
+  int* const s_fallback = reinterpret_cast<int*>(slot3 + kRope);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 31, half = lane >> 5, gi = lane & 15;
+  const int b = t / a.n_q;
+
+  int L = a.seq_lens[b];
+  L = max(0, min(L, a.max_pages * 64));
+  const int i0 = split * a.split_len;
+  const int cnt = FUSED ? own_cnt : max(0, min(a.split_len, a.top_k - i0));
+  const int n_tiles = (cnt + kTileRows - 1) / kTileRows;
+  const bool whole = FUSED ? direct : a.n_splits == 1;  // the result is the output itself
+  const int* bt = a.block_table + (size_t)b * a.max_pages;
+
+  // ---------------------------------------------------------------- rows of this slice, q^T operands
+  // The index entries and then the page ids are loaded (two dependent memory
+  // latencies); the q loads are issued while the page ids are in flight, so
+  // they overlap with the rows' resolution and with the first tiles' loads.
+  if (tid == 0) *s_fallback = FUSED && cnt > 0 ? rows[0] : 0x7fffffff;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  constexpr int RPT = ROWS / NT;  // rows per thread: one pass covers any slice
+  const int n_rows = n_tiles * kTileRows;
+  int pos_v[RPT], page_v[RPT];
+  if (FUSED) {
+    // rows already resolved by the caller: only the last tile's tail is skipped
+    if (tid < n_rows - cnt) rows[cnt + tid] = -1;
+  } else if (cnt > 0) {
+    const int32_t* ip = a.idx + (size_t)t * a.top_k + i0;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int i = tid + r * NT;
+      const int v = ip[min(i, cnt - 1)];
+      pos_v[r] = i < cnt ? v : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const bool valid = pos_v[r] >= 0 && pos_v[r] < L;
+      page_v[r] = bt[valid ? pos_v[r] >> 6 : 0];
+    }
+  }
+
+  const int head = 32 * wid + n;
+  const bool head_ok = head < a.H;
+  bf16x8 qb[KS];
+  {
+    // padded heads (head >= H) run on head 0's query; nothing of theirs is stored
+    const bf16x8* qp =
+        reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + ((size_t)t * a.H + (head_ok ? head : 0)) * 576);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qb[k] = qp[2 * k + half];
+  }
+  // the page ids are first used here, after the q loads have been issued
+  if (!FUSED) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) asm volatile("" : "+v"(page_v[r]) : : "memory");
+  }
+
+  if (!FUSED && cnt > 0) {
+    int fb = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int i = tid + r * NT;
+      if (i < n_rows) {
+        const bool valid = pos_v[r] >= 0 && pos_v[r] < L;
+        const int rr = valid ? min(max(page_v[r], 0), a.num_pages - 1) * 64 + (pos_v[r] & 63) : -1;
+        rows[i] = rr;
+        if (valid) fb = min(fb, rr);
+      }
+    }
+    if (fb != 0x7fffffff) atomicMin(s_fallback, fb);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const int fallback = __builtin_amdgcn_readfirstlane(*s_fallback);  // uniform: kept in a scalar register
+  const int tiles = fallback != 0x7fffffff ? n_tiles : 0;
+  // row read in place of skipped entries (and by the prologue's loads past
+  // the last tile): a valid row of the slice, else the pool's first row
+  const int fb_row = tiles > 0 ? fallback : 0;
+
+  // ---------------------------------------------------------------- gathers
+  // Wave w issues loads w, w+NW, ... of a tile; lane l of load i copies row
+  // 8(i%4) + l/8, chunk 8(i/4) + ((l & 7) ^ f(row)).  With NW dividing 4 a
+  // lane meets only 4/NW distinct rows, and f(row) depends on l alone, so
+  // each load is one per-row base address plus an immediate offset.
+  const int c_lane = (lane & 7) ^ swz(lane >> 3);
+  auto ring = [&](int tile) -> char* {
+    const int i = tile & 3;
+    return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3;
+  };
+  constexpr int RPW = 4 / NW;
+  // the row ids a lane's loads of a tile use (read ahead of the loads)
+  auto tile_rows = [&](int tile, int (&pr)[4]) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) pr[r] = rows[tile * kTileRows + 8 * (wid + NW * r) + (lane >> 3)];
+  };
+  // With four waves a lane copies one row per tile (tile < tiles unless it
+  // is a prologue load).  The loads go through a buffer resource over the
+  // pool with one 1152-byte record per latent row: the row is the index, the
+  // lane's chunk the per-lane offset and load k's 128-byte step the
+  // wave-uniform offset, so a load costs no per-lane address arithmetic.
+  static_assert(RPW == 1, "one row per lane and tile");
+  const uint32_t pool_rows = (uint32_t)min((long long)a.num_pages * 64, 0xffffffffll);
+  const auto kv_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kv), (short)1152, (int)pool_rows, 0x00020000);
+  const uint32_t c16 = 16 * c_lane;
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+  auto tile_row = [&](int tile, const int (&pr)[4]) -> int { return (pr[0] >= 0 && tile < tiles) ? pr[0] : fb_row; };
+  // load k of this wave into the tile at dst (= its slot + 1 KiB x wave)
+  auto load_one = [&](char* dst, int row, int k) {
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + 1024 * NW * k), 16, row, c16, 128 * k, 0, 0);
+  };
+  auto issue = [&](int tile) {
+    int pr[4];
+    tile_rows(tile, pr);
+    const int row = tile_row(tile, pr);
+    char* dst = ring(tile) + 1024 * wid_s;
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) load_one(dst, row, k);
+  };
+
+  // ---------------------------------------------------------------- operand reads
+  // Byte offsets inside a tile (tile_off with the swizzle resolved per lane):
+  // logits k-step k of lane (n, half) = row n, chunk 2k + half
+  //   = (abase ^ 32 (k % 4)) + 4096 (k / 4);
+  // output column tile m (32 columns) at k-block kk: the 16-lane group reads
+  // rows r0..r0+3 and r0+8..r0+11 (r0 = 16 kk + tr_row) of two adjacent
+  // chunks, lane gi receiving one column, four consecutive rows per read; the
+  // low read sits at (pbase ^ 64 (m % 2)) + 4096 (m / 2) + 2048 kk and the
+  // high one 1024 bytes further.  This wave's column tiles are
+  // m = 4 wid .. 4 wid + 3.  (The swizzle only permutes chunks inside an
+  // aligned group of 8 or 4, so the per-step offsets are XORs of one base;
+  // slot bases are multiples of 128 and keep those bits clear.)
+  int abase, pbase;
+  {
+    const int tr_row = 4 * half + (gi >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
+    abase = 16 * (64 * (n >> 3) + 8 * (n & 7) + (half ^ swz(n)));
+    pbase = 16 * (8 * tr_row + (tr_chunk ^ swz(tr_row))) + 8 * (gi & 1);
+  }
+  // The LDS operand reads are issued as instructions of their own: the wait
+  // pass cannot tell an LDS read from the direct-to-LDS loads in flight into
+  // other slots and would drain them all first.  Their results are awaited
+  // explicitly before use.
+  auto lds_addr = [](const char* p) -> uint32_t { return (uint32_t)(uintptr_t)(const lds_void*)p; };
+  // transposed pair of this wave's column tile mm (0..3) at k-block kk
+  auto pv_issue = [&](uint32_t c, int kk, int mm, bf16x4& lo, bf16x4& hi) {
+    const uint32_t p = (c + pbase) ^ (64 * (mm & 1));
+    switch (4096 * (mm >> 1) + 2048 * kk) {
+#define SLI_TR_CASE(OFF)                                                                   \
+  case OFF:                                                                                \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(p), "i"(OFF));     \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(p), "i"(OFF + 1024)); \
+    break;
+      SLI_TR_CASE(0) SLI_TR_CASE(2048) SLI_TR_CASE(4096) SLI_TR_CASE(6144)
+#undef SLI_TR_CASE
+    }
+  };
+  // P^T operand of head block hb at k-block kk (16 bytes per lane)
+  const uint32_t p_lane = lds_addr(pbuf) + 16 * lane;
+  auto pp_issue = [&](int kk, int hb, bf16x8& v) {
+    switch (1024 * (2 * hb + kk)) {
+#define SLI_PP_CASE(OFF)                                                             \
+  case OFF:                                                                          \
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p_lane), "i"(OFF)); \
+    break;
+      SLI_PP_CASE(0) SLI_PP_CASE(1024) SLI_PP_CASE(2048) SLI_PP_CASE(3072)
+      SLI_PP_CASE(4096) SLI_PP_CASE(5120) SLI_PP_CASE(6144) SLI_PP_CASE(7168)
+#undef SLI_PP_CASE
+    }
+  };
+  // rescale of this wave's heads to publish with the weights (sm_finish)
+  bool pub_need = false;
+  float pub_alpha = 1.f;
+
+  f32x16 o[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) o[i] = (f32x16){};
+  float m_run = -1e30f, l_run = 0.f;
+  const float sl2 = a.sm_scale * kLog2e;
+  bf16x8 pb[2];  // P^T of the previous tile (k-blocks 0 and 1)
+  pb[0] = pb[1] = (bf16x8){};
+
+  // Online softmax of one tile's S^T, in stages that the output product of
+  // the previous tile interleaves with its MFMAs.  This lane owns head n and
+  // positions 8(v/4) + 4 half + v%4.  Entries past the slice or invalid were
+  // gathered from a valid row of the slice, so their (finite) logits may
+  // enter the maximum, which is only the reference of the exponentials; their
+  // weights are zeroed.  The running reference is raised (and the
+  // accumulators rescaled) only when some head's tile maximum exceeds it by
+  // more than 2^8, so weights stay below 256 (harmless in fp32 sums and bf16
+  // operands) and most tiles skip the rescale.
+  struct Sm {
+    float mt;        // tile maximum, scaled (both lane halves)
+    float m_new, alpha, rs;
+    bool need;       // the reference moves (wave-uniform)
+    bf16x8 p[2];     // weights, the next output product's B operands
+  } sm;
+  // the two lane halves hold the same head: combine across them
+  auto halves = [](float v, bool is_max) -> float {
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return is_max ? fmaxf(a, b) : a + b;
+  };
+  // The logits stay unscaled in sv: the scale (> 0) is applied to the
+  // maximum and folded into the exponentials' argument.
+  auto sm_stage = [&](int st, const f32x16& sv) {
+    if (st == 0) {
+      sm.mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    } else if (st == 1) {
+      const float m = fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15])));
+      sm.mt = fmaxf(sm.mt, m);
+    } else if (st == 2) {
+      sm.mt *= sl2;
+    } else if (st == 3) {
+      sm.mt = halves(sm.mt, true);
+      sm.need = __ballot(sm.mt > m_run + 8.f) != 0;
+      sm.m_new = sm.need ? fmaxf(m_run, sm.mt) : m_run;
+      sm.alpha = __builtin_amdgcn_exp2f(m_run - sm.m_new);
+      sm.rs = 0.f;
+    } else if (st >= 4 && st < 12) {
+      const int v = 2 * (st - 4);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], sl2, -sm.m_new));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v + 1], sl2, -sm.m_new));
+      sm.rs += p0 + p1;
+      sm.p[v >> 3][v & 7] = (__bf16)p0;
+      sm.p[v >> 3][(v & 7) + 1] = (__bf16)p1;
+    }
+  };
+  constexpr int SM_STAGES = 12;
+  // finishes the tile's softmax once the previous output product is done:
+  // zero the weights of invalid entries (rare), rescale, fold the sum
+  auto sm_finish = [&](uint32_t vmask) {
+    if (vmask != 0xffffffffu) {
+      float rs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int pos = 8 * (v >> 2) + 4 * half + (v & 3);
+        const float p = ((vmask >> pos) & 1u) ? (float)sm.p[v >> 3][v & 7] : 0.f;
+        sm.p[v >> 3][v & 7] = (__bf16)p;
+        rs += p;
+      }
+      sm.rs = rs;
+    }
+    // The accumulators of this wave's heads are held by every wave: the
+    // rescale factor is published with the weights and applied by each wave
+    // before the tile's output product (not at all while nothing has been
+    // accumulated).
+    pub_need = sm.need && __ballot(m_run > -1e29f) != 0;
+    pub_alpha = sm.alpha;
+    if (sm.need) {
+      l_run *= sm.alpha;
+      m_run = sm.m_new;
+    }
+    l_run += halves(sm.rs, false);
+    pb[0] = sm.p[0];
+    pb[1] = sm.p[1];
+  };
+
+  // Writes the weights and rescale factors of `tile` (finished in registers
+  // by sm_finish) where every wave reads them; the caller waits for the
+  // writes and a barrier makes them visible.
+  auto publish = [&](int tile) {
+    const uint32_t pa = lds_addr(pbuf) + 2048 * wid + 16 * lane;
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" : : "v"(pa), "v"(pb[0]), "v"(pb[1]) : "memory");
+    const uint32_t ra = lds_addr(ring(tile)) + kRope;
+    if (pub_need && half == 0)
+      asm volatile("ds_write_b32 %0, %1" : : "v"(ra + 4 * (32 * wid + n)), "v"(pub_alpha) : "memory");
+    if (lane == 0) asm volatile("ds_write_b32 %0, %1 offset:512" : : "v"(ra + 4 * wid), "v"(pub_need ? 1 : 0) : "memory");
+  };
+  // Rescales the accumulators of the head blocks whose reference moved with
+  // `tile` (after the barrier that follows publish).
+  auto apply_rescale = [&](int tile) {
+    const uint32_t ra = lds_addr(ring(tile)) + kRope;
+    i32x4 fl;
+    asm volatile("ds_read_b128 %0, %1 offset:512\n\ts_waitcnt lgkmcnt(0)" : "=v"(fl) : "v"(ra) : "memory");
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      if (__builtin_amdgcn_readfirstlane(fl[hb]) != 0) {
+        float al;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(al) : "v"(ra + 4 * (32 * hb + n)) : "memory");
+        // (the accumulators stay in the accumulation registers around the
+        // scaling; without the pins the allocator moves them and spills q)
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          asm volatile("" : "+a"(o[4 * mm + hb]));
+          o[4 * mm + hb] *= al;
+          asm volatile("" : "+a"(o[4 * mm + hb]));
+        }
+      }
+    }
+  };
+
+  // logits S^T[pos, head] of one tile (one accumulator chain: a second one
+  // would not fit beside q and the output accumulators).  The operand reads
+  // are instructions of their own, like the transposed reads below.
+  auto av_issue = [&](uint32_t c, int k, bf16x8& v) {
+    const uint32_t p = (c + abase) ^ (32 * (k & 3));
+    switch (4096 * (k >> 2)) {
+#define SLI_AV_CASE(OFF)                                                            \
+  case OFF:                                                                         \
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(OFF));      \
+    break;
+      SLI_AV_CASE(0) SLI_AV_CASE(4096) SLI_AV_CASE(8192) SLI_AV_CASE(12288) SLI_AV_CASE(16384)
+      SLI_AV_CASE(20480) SLI_AV_CASE(24576) SLI_AV_CASE(28672) SLI_AV_CASE(32768)
+#undef SLI_AV_CASE
+    }
+  };
+  auto logits = [&](const char* C) -> f32x16 {
+    const uint32_t c = lds_addr(C);
+    bf16x8 av[KS];
+    f32x16 s0 = (f32x16){};
+#pragma unroll
+    for (int k = 0; k < PDL; ++k) av_issue(c, k, av[k]);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (k + PDL < KS) av_issue(c, k + PDL, av[k + PDL]);
+      switch (min(PDL, KS - 1 - k)) {
+#define SLI_AV_WAIT(N)                                                              \
+  case N:                                                                           \
+    asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(av[k]));                         \
+    break;
+        SLI_AV_WAIT(0) SLI_AV_WAIT(1) SLI_AV_WAIT(2) SLI_AV_WAIT(3) SLI_AV_WAIT(4)
+#undef SLI_AV_WAIT
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return s0;
+  };
+  // Output product O^T[d, head] += C^T[d, pos] . P^T[pos, head] of the
+  // previous tile (do_pv) for this wave's 128 columns and every head, with the
+  // current tile's softmax stages (do_sm) interleaved between its MFMAs.  MFMA
+  // j: k-block kk = j / 16, column tile mm = (j / 4) % 4, head block
+  // hb = j % 4; the read schedule and its waits are described at
+  // sfa_pv_wait.
+  auto outprod = [&](const char* C, bool do_pv, const f32x16& sv, bool do_sm, int ld_tile, const int (&pr)[4]) {
+    const uint32_t c = lds_addr(C) + 8192 * wid;
+    const int ld_row = tile_row(ld_tile, pr);
+    const bool do_ld = ld_tile < tiles;
+    char* const ld_dst = ring(ld_tile) + 1024 * wid_s;
+    bf16x4 lo[8], hi[8];
+    bf16x8 pv[2][4];
+    if (do_pv) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) pp_issue(0, hb, pv[0][hb]);
+#pragma unroll
+      for (int pi = 0; pi < kPvAhead; ++pi) pv_issue(c, 0, pi, lo[pi], hi[pi]);
+    }
+    static_for<PVS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int kk = j >> 4, mm = (j >> 2) & 3, hb = j & 3, pi = 4 * kk + mm;
+      if (do_pv) {
+        if constexpr (hb == 0 && pi + kPvAhead < 8)
+          pv_issue(c, (pi + kPvAhead) >> 2, (pi + kPvAhead) & 3, lo[pi + kPvAhead], hi[pi + kPvAhead]);
+        constexpr int w = sfa_pv_outstanding(kPvAhead, j);
+        asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo[pi]), "+v"(hi[pi]), "+v"(pv[kk][hb]) : "i"(w));
+        const bf16x8 cv = (bf16x8){lo[pi][0], lo[pi][1], lo[pi][2], lo[pi][3], hi[pi][0], hi[pi][1], hi[pi][2], hi[pi][3]};
+        o[4 * mm + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv, pv[kk][hb], o[4 * mm + hb], 0, 0, 0);
+        SLI_PIN_A(o[4 * mm + hb]);
+        if constexpr (kk == 0 && mm == 3) pp_issue(1, hb, pv[1][hb]);
+      }
+      if constexpr (j % 2 == 1 && j / 2 < SM_STAGES) {
+        if (do_sm) sm_stage(j / 2, sv);
+      }
+      // The next tile's loads go between these independent MFMAs, one every
+      // third step (four waves then issue one about every 25 cycles, within
+      // the ~15 cycles per direct-to-LDS load the CU accepts).
+      if constexpr (j % 3 == 1 && j / 3 < DPW) {
+        if (do_ld) load_one(ld_dst, ld_row, j / 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---------------------------------------------------------------- main loop
+  // Iteration t: wait for tile t, load tile t + 2 into the slot of tile t - 2,
+  // logits of tile t, then the output product of tile t - 1 with tile t's
+  // softmax interleaved.  Two tiles are in flight while two are consumed.
+  // The prologue always issues tiles 0 and 1 (past the last tile with the
+  // fallback row), so the count is exact: waiting for all but those loads
+  // completes the q loads issued before them, and the loop needs no wait for q.
+  issue(0);
+  issue(1);
+  SLI_WAIT_VMCNT(2 * DPW);
+  // row ids of the tile loaded next, and the valid-entry mask of the tile
+  // consumed next, both read one iteration ahead
+  int pr_next[4] = {0, 0, 0, 0};
+  if (2 < tiles) tile_rows(2, pr_next);
+  uint32_t vmask = tiles > 0 ? (uint32_t)__ballot(rows[n] >= 0) : 0u;
+  auto step = [&](int tile, bool prev) {
+    if (tile + 1 < tiles) {
+      SLI_WAIT_VMCNT(DPW);
+    } else {
+      SLI_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    // every wave is past tile - 2's output product (the weights buffer is
+    // free) and tile - 1's logits (its rope columns are free)
+    if (prev) {
+      publish(tile - 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      apply_rescale(tile - 1);
+    }
+    const int pr[4] = {pr_next[0], pr_next[1], pr_next[2], pr_next[3]};
+    const f32x16 sv = logits(ring(tile));
+    if (tile + 3 < tiles) tile_rows(tile + 3, pr_next);
+    const uint32_t vm_next = tile + 1 < tiles ? (uint32_t)__ballot(rows[(tile + 1) * kTileRows + n] >= 0) : 0u;
+    outprod(ring(tile - 1), prev, sv, true, tile + 2, pr);
+    sm_finish(vmask);
+    vmask = vm_next;
+  };
+  if (tiles > 0) step(0, false);
+#pragma unroll 1
+  for (int tile = 1; tile < tiles; ++tile) step(tile, true);
+  if (tiles > 0) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    publish(tiles - 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    apply_rescale(tiles - 1);
+    outprod(ring(tiles - 1), true, (f32x16){}, false, tiles, pr_next);
+  }
+
+  // ---------------------------------------------------------------- write out
+  // 1 / sum of every head reaches every wave through the weights buffer; the
+  // output (every head, this wave's 128 columns) is staged in LDS, head block
+  // hb in slot hb (rows padded to 1040 bytes), so that each global store
+  // writes one whole 1 KiB head row.
+  SLI_WAIT_VMCNT(0);  // (prologue loads past the last tile included)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();  // every wave is done with the last tile and the weights
+  float* const s_inv = reinterpret_cast<float*>(pbuf);
+  if (half == 0) s_inv[32 * wid + n] = l_run > 0.f ? 1.f / l_run : 0.f;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  constexpr int kStageRow = 1040;
+  {
+    float inv[NW];
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) inv[hb] = s_inv[32 * hb + n];
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * (4 * wid + mm) + 8 * q4 + 4 * half;
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[4 * mm + hb][4 * q4 + i] * inv[hb]);
+          *reinterpret_cast<bf16x4*>(ring(hb) + n * kStageRow + 2 * d) = v4;
+        }
+  }
+  const size_t th = (size_t)t * a.H + head;
+  const size_t ps = ((size_t)t * a.n_splits + split) * a.H + head;
+  if (head_ok && half == 0) {
+    if (whole) {
+      if (a.lse) a.lse[th] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    } else if (FUSED) {
+      xstore64(reinterpret_cast<uint64_t*>(a.part_ml + 2 * ps),
+               (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32));
+    } else {
+      a.part_ml[2 * ps] = m_run;
+      a.part_ml[2 * ps + 1] = l_run;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();  // head block wid's rows were staged by every wave
+  const char* stage = ring(wid);
+  const int rows_out = min(32, a.H - 32 * wid);
+  __bf16* obase = whole ? static_cast<__bf16*>(a.out) + ((size_t)t * a.H + 32 * wid) * 512
+                        : a.part_o + (((size_t)t * a.n_splits + split) * a.H + 32 * wid) * 512;
+  if (FUSED && !whole) {
+    // partials for the merge, written through to memory
+    const uint32_t ob = (uint32_t)((obase - a.part_o) * 2);
+#pragma unroll 4
+    for (int r = 0; r < rows_out; ++r)
+      xstore128(a.part_o, ob + (uint32_t)r * 1024u + 16u * lane,
+                *reinterpret_cast<const i32x4*>(stage + r * kStageRow + 16 * lane));
+    return;
+  }
+#pragma unroll 4
+  for (int r = 0; r < rows_out; ++r) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(stage + r * kStageRow + 16 * lane);
+    *reinterpret_cast<i32x4*>(obase + (size_t)r * 512 + 8 * lane) = v;
+  }
+}
+
+// bf16 latent rows, every head of the token in one workgroup: work item =
+// (token, split) of blockIdx.  The hardware deals workgroups round-robin
+// over the 8 XCDs (id % 8); XCD x takes a contiguous range of tokens with all
+// of their splits, so the splits of a token share one L2 for the token's q
+// (and neighbouring prefill tokens, which select mostly the same rows, share
+// it for the rows).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sfa_bf16_kernel(const SfaArgs a) {
+  // four ring slots as separate LDS objects: the compiler can then tell a read
+  // of one slot from a direct-to-LDS load into another and does not make the
+  // read wait for every load in flight
+  __shared__ __attribute__((aligned(128))) char slot0[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char slot1[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char slot2[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char slot3[kTileBytes];
+  // P^T operands of one tile for every head: 16 bytes per (head block, k-block, lane)
+  __shared__ __attribute__((aligned(128))) char pbuf[NW * 2 * 64 * 16];
+  __shared__ int rows[kMaxSplitRows];
+  const int x = blockIdx.x & 7, g = blockIdx.x >> 3;
+  const int tpx = (a.T + 7) / 8;
+  const int t = x * tpx + g / a.n_splits;
+  const int split = g % a.n_splits;
+  if (t >= a.T) return;
+  sfa_bf16_body<NW, kMaxSplitRows, false>(a, SfaBf16Lds{slot0, slot1, slot2, slot3, pbuf, rows}, t, split);
+}
+
+// Merges the split partials of one (token, head).  Split s holds its output
+// normalised by its own sum, O_s, with (m_s, l_s); with w_s = 2^(m_s - M) l_s,
+// o = sum_s w_s O_s / sum_s w_s.  A thread takes NC groups of 8 columns of
+// head h (columns 8 NC l .. 8 NC l + 8 NC - 1).  Splits are taken 8 at a time
+// with every load of the group in flight at once (one memory latency per
+// group); a later group rescales the running sums to its larger maximum.  The
+// partials of token t sit in slots 0 .. S-1 of its a.n_splits slots.
+template <bool FUSED, int NC = 1>
+__device__ __forceinline__ void sfa_merge_head(const SfaArgs& a, const int t, const int h, const int l, const int S) {
+  constexpr int G = 8;
+  const size_t row0 = (size_t)t * a.n_splits * a.H + h;  // (token, slot 0, head); slots are H rows apart
+  float M = -INFINITY, den = 0.f;
+  float acc[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[c][j] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += G) {
+    float2 ml[G];
+    bf16x8 v[G][NC];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int s = min(s0 + i, S - 1);
+      const size_t row = row0 + (size_t)s * a.H;
+      if constexpr (FUSED) {
+        const uint64_t w = xload64(reinterpret_cast<const uint64_t*>(a.part_ml + 2 * row));
+        ml[i] = make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          v[i][c] = __builtin_bit_cast(bf16x8, xload128(a.part_o, (uint32_t)((row * 512 + 8 * (NC * l + c)) * 2)));
+      } else {
+        ml[i] = *reinterpret_cast<const float2*>(a.part_ml + 2 * row);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) v[i][c] = *reinterpret_cast<const bf16x8*>(a.part_o + row * 512 + 8 * (NC * l + c));
+      }
+    }
+    float Mg = M;
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (s0 + i < S && ml[i].y > 0.f) Mg = fmaxf(Mg, ml[i].x);
+    Mg = Mg == -INFINITY ? 0.f : Mg;  // nothing valid so far: every weight is 0
+    const float r = exp2f(M - Mg);     // rescale of the earlier groups (0 when none)
+    den *= r;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[c][j] *= r;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float wgt = (s0 + i < S && ml[i].y > 0.f) ? exp2f(ml[i].x - Mg) * ml[i].y : 0.f;
+      den += wgt;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[c][j] += wgt * (float)v[i][c][j];
+    }
+    M = den > 0.f ? Mg : -INFINITY;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (__bf16)(acc[c][j] * inv);
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.out) + ((size_t)t * a.H + h) * 512 + 8 * (NC * l + c)) = r;
+  }
+  if (a.lse && l == 0) a.lse[(size_t)t * a.H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+}  // namespace sli

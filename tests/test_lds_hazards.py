@@ -69,3 +69,50 @@ def test_lds_writes_count_without_destination():
         v_add_f32_e32 v30, v10, v31
     """)
     assert found == []
+
+
+def test_loop_carried_read_is_checked_at_the_loop_head():
+    """A read issued at the end of a loop body and used at the loop head of
+    the next iteration, before any wait."""
+    found = _scan("""
+        s_mov_b32 s0, 0
+    .LBB0_1:
+        v_add_f32_e32 v30, v10, v31
+        s_waitcnt lgkmcnt(0)
+        ds_read_b32 v10, v1
+        s_add_u32 s0, s0, 1
+        s_cbranch_scc1 .LBB0_1
+        s_waitcnt lgkmcnt(0)
+        s_endpgm
+    """)
+    assert [r for _, r in found] == [("v", 10)]
+
+
+def test_wait_on_a_skipped_branch_clears_nothing_after_the_join():
+    found = _scan("""
+        ds_read_b128 v[10:13], v1
+        s_cbranch_vccz .LBB0_2
+        s_waitcnt lgkmcnt(0)
+    .LBB0_2:
+        v_mov_b32_e32 v30, v12
+        s_waitcnt lgkmcnt(0)
+        v_mov_b32_e32 v31, v13
+        s_endpgm
+    """)
+    assert [r for _, r in found] == [("v", 12)]
+
+
+def test_code_after_the_first_endpgm_is_scanned():
+    from sparse_attention_li_amd import lds_hazards as lh
+    asm = """_ZN3sli1kEv:
+    s_cbranch_vccz .LBB0_3
+    s_endpgm
+.LBB0_3:
+    ds_read_b32 v10, v1
+    v_mov_b32_e32 v30, v10
+    s_waitcnt lgkmcnt(0)
+    s_endpgm
+.Lfunc_end0:
+"""
+    found = lh.check_asm(asm, ("_ZN3sli1kEv",))
+    assert [r for _, _, r in found] == ["v10"]
