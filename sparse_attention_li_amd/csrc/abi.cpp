@@ -203,7 +203,7 @@ StepLayout step_layout(int B, int max_pages, int H, int top_k) {
 bool step_fused(int B, int q_per_seq, int q_dtype, int k_dtype, int kv_dtype, int H, int max_pages) {
   if (q_per_seq != 1 || q_dtype != LI_BF16 || k_dtype != LI_BF16 || kv_dtype != LI_BF16 || H != 128) return false;
   const long long ncm = std::max<long long>(1, ((long long)max_pages * 64 + 4095) / 4096);
-  return ncm <= 64 && (long long)B * ncm <= device_cus();
+  return ncm <= 64 && (long long)(B + 7) / 8 * 8 * ncm <= device_cus();
 }
 
 
@@ -450,7 +450,9 @@ li_status li_decode_step(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq
   a.k_mx = false;
   a.idx_out = idx_out;
   a.spin_max = spin_max();
-  a.xcd_local = 0;
+  // a request's chunks on one XCD: its query (read by every chunk's
+  // attention) is fetched into that XCD's L2 once, not once per chunk
+  a.xcd_local = 1;
   {
     size_t o = 0;
     a.counters = reinterpret_cast<uint32_t*>(ws + o);

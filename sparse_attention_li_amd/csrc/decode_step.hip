@@ -131,7 +131,9 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
     const int L = max(0, min(a.seq_lens[b], a.max_pages * 64));
     const uint32_t n_chunks = (uint32_t)max(1, (L + kStepChunk - 1) / kStepChunk);
     const uint32_t ncm = (uint32_t)a.n_chunks_max;
-    const int c = (int)((blockIdx.x % ncm + ncm - (uint32_t)b % ncm) % ncm);  // the indexer's (spread) block layout
+    // the chunk of this workgroup, in the indexer's block layout
+    const int c = a.xcd_local ? (int)((blockIdx.x >> 3) % ncm)
+                              : (int)((blockIdx.x % ncm + ncm - (uint32_t)b % ncm) % ncm);
     // 2. attention over the rows this workgroup wrote
     const bool direct = st == kBodyAll || n_chunks == 1;
     const SfaBf16Lds lds{reinterpret_cast<char*>(X), reinterpret_cast<char*>(X + kTileBytes),
@@ -175,7 +177,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
 }
 
 hipError_t launch_decode_step(const StepArgs& s, hipStream_t stream) {
-  const long long blocks = (long long)s.idx.B * s.idx.n_chunks_max;
+  const long long blocks = s.idx.xcd_local ? (long long)((s.idx.B + 7) / 8) * 8 * s.idx.n_chunks_max
+                                           : (long long)s.idx.B * s.idx.n_chunks_max;
   hipLaunchKernelGGL(li_step_kernel, dim3((unsigned)blocks), dim3(kStepWaves * 64), 0, stream, s);
   return hipGetLastError();
 }
