@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_li.so")
 
-SOURCES = ["abi.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip", "noalloc.hip",
+SOURCES = ["abi.cpp", "shapes.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip", "noalloc.hip",
            "decode_step.hip"]
 
 HIP_FLAGS = [

@@ -35,26 +35,6 @@ static hipError_t launch_one(const IdxDecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Positions per workgroup.  4096 (eight waves, one workgroup per CU) when
-// the grid still gives every CU a workgroup: each CU then streams the same
-// amount and the request's chunks finish together.  Smaller chunks (four
-// waves, two workgroups per CU) for small batches, and for bf16 two-token
-// calls, whose keys and key ring would not fit beside each other in LDS.
-int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus) {
-  const long long maxlen = (long long)max_pages * 64;
-  auto wgs = [&](long long ch) { return (long long)B * ((maxlen + ch - 1) / ch); };
-  if ((n_q == 1 || fp8) && wgs(4096) >= cus) return 4096;
-  return wgs(1024) > 2LL * cus ? 2048 : 1024;
-}
-
-// XCD-local block layout when the grid takes several rounds of the chip (one
-// workgroup per CU counted), a request's chunks fit in one XCD's CUs at once,
-// and there are enough requests (>= 2 per XCD) to balance the XCDs.
-bool idx_decode_xcd_local(int B, int n_chunks_max, int chunk, int cus) {
-  (void)chunk;
-  return B >= 16 && n_chunks_max <= cus / 8 && (long long)B * n_chunks_max > cus;
-}
-
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream) {
   if (chunk == 1024) {
     if (a.n_q == 1) return fp8 ? launch_one<1, 4, 1024, true>(a, stream) : launch_one<1, 4, 1024, false>(a, stream);

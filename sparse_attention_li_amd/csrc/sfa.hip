@@ -399,8 +399,6 @@ static hipError_t launch_sfa_bf16(const SfaArgs& a, hipStream_t stream) {
   return e != hipSuccess ? e : launch_combine(a, stream);
 }
 
-int sfa_heads_per_block(int H, bool fp8) { return (fp8 || H <= 64) ? (H <= 32 ? 32 : 64) : 128; }
-
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream) {
   if (fp8 && a.rope_bf16)
     return a.H <= 32 ? launch_sfa_blocks<1, true, true>(a, stream) : launch_sfa_blocks<2, true, true>(a, stream);

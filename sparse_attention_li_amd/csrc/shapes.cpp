@@ -1,0 +1,31 @@
+// Launch-shape choices of the kernels (plain host code, no device code, so
+// the C ABI's host logic can be built and checked on a machine without a GPU).
+#include "launch.h"
+
+namespace sli {
+
+// Positions per workgroup.  4096 (eight waves, one workgroup per CU) when
+// the grid still gives every CU a workgroup: each CU then streams the same
+// amount and the request's chunks finish together.  Smaller chunks (four
+// waves, two workgroups per CU) for small batches, and for bf16 two-token
+// calls, whose keys and key ring would not fit beside each other in LDS.
+int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus) {
+  const long long maxlen = (long long)max_pages * 64;
+  auto wgs = [&](long long ch) { return (long long)B * ((maxlen + ch - 1) / ch); };
+  if ((n_q == 1 || fp8) && wgs(4096) >= cus) return 4096;
+  return wgs(1024) > 2LL * cus ? 2048 : 1024;
+}
+
+// XCD-local block layout when the grid takes several rounds of the chip (one
+// workgroup per CU counted), a request's chunks fit in one XCD's CUs at once,
+// and there are enough requests (>= 2 per XCD) to balance the XCDs.
+bool idx_decode_xcd_local(int B, int n_chunks_max, int chunk, int cus) {
+  (void)chunk;
+  return B >= 16 && n_chunks_max <= cus / 8 && (long long)B * n_chunks_max > cus;
+}
+
+// Heads per attention workgroup: every head of the token (up to 128) for
+// bf16 rows, blocks of up to 64 heads for FP8 rows or small head counts.
+int sfa_heads_per_block(int H, bool fp8) { return (fp8 || H <= 64) ? (H <= 32 ? 32 : 64) : 128; }
+
+}  // namespace sli
