@@ -73,10 +73,12 @@ typedef enum { LI_BF16 = 0, LI_FP8 = 1, LI_MXFP8 = 2, LI_FP8_ROPE_BF16 = 3 } li_
 #define LI_VALUE_DIM 512
 #define LI_MAX_TOP_K 2048
 
-/* Version string of the library (static storage). */
+/* Version string of the library (static storage).  Library housekeeping:
+ * no passage of the pages defines it. */
 const char* li_version(void);
 
-/* Message of the last failing call on this thread (static thread-local storage). */
+/* Message of the last failing call on this thread (static thread-local
+ * storage).  Library housekeeping: no passage of the pages defines it. */
 const char* li_last_error(void);
 
 /*
@@ -84,25 +86,39 @@ const char* li_last_error(void);
  * sleep each) a cross-workgroup exchange wait of li_score_topk makes before it
  * gives up and takes its exact fallback; default 20000, a negative value
  * restores the default.  Lowering it forces the fallbacks, which changes
- * timing only, never results.  Process-wide, read at each call.
+ * timing only, never results.  Process-wide, read at each call.  The exchange
+ * is this library's way of keeping the selection on chip ("Day0 Inference
+ * Support and Performance Optimization for New-Architecture LLMs", sec. 4:
+ * Top-K without writing the scores back); the pages define no such knob.
  */
 void li_set_exchange_patience(int32_t polls);
 
 /*
  * Bytes of workspace li_score_topk needs for this geometry.  max_pages bounds
- * every L_b (L_b <= max_pages*64).  Returns 0 for invalid arguments.
+ * every L_b (L_b <= max_pages*64).  Returns 0 for invalid arguments.  The
+ * workspace holds the on-chip selection's exchange state, not scores (the
+ * pages keep the score matrix out of memory: "Day0 Inference Support and
+ * Performance Optimization for New-Architecture LLMs", sec. 4).
  */
 size_t li_score_topk_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_t max_pages, int32_t top_k);
 
 /*
  * Zero-fills a workspace on `stream` with a kernel (no hipMemset, so it may be
  * captured in a HIP graph).  A workspace must be zero before its first use by
- * li_score_topk; every li_score_topk call leaves it zero again.
+ * li_score_topk; every li_score_topk call leaves it zero again.  Library
+ * housekeeping for the workspace above: no passage of the pages defines it.
  */
 li_status li_workspace_zero(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * li_score_topk -- fused indexer score + Top-K selection.
+ * li_score_topk -- fused indexer score + Top-K selection.  The score is the
+ * per-head q.k, ReLU, and the head-weighted sum over the 64 indexer heads;
+ * the selection keeps the top_k positions per query token, on chip ("Day-0
+ * Inference Adaptation and Optimization for Hybrid Attention Architectures",
+ * sec. 1 and 3; "Optimizing Inference for Hybrid Attention LLMs", sec. 3.1;
+ * "Day0 Inference Support and Performance Optimization for New-Architecture
+ * LLMs", sec. 4).  The FP8 forms follow the quantised indexer layouts of
+ * "Optimizing Inference for Hybrid Attention LLMs", sec. 4 table.
  *
  *   q         [T,64,128]  indexer query; LI_BF16 bits, or LI_FP8 E4M3 codes with
  *   q_scales  [T,64,4]    E8M0 scales (one per 32 consecutive elements; LI_FP8 only,
@@ -164,12 +180,22 @@ li_status li_score_topk_noalloc(int32_t num_seqs, int32_t q_per_seq, const int32
                                 void* stream);
 
 /*
- * Bytes of workspace sfa_decode / sfa_prefill need (split partial results).
+ * Bytes of workspace sfa_decode / sfa_prefill need: the partial results when
+ * a token's index row is split over several workgroups (our decomposition of
+ * the attention of "Day0 Inference Adaptation and Performance Optimization
+ * for a Sparse Hybrid Architecture LLM", sec. 2.1; the pages do not split).
  */
 size_t sfa_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t top_k);
 
 /*
- * sfa_decode -- sparse MLA attention over the selected latent rows.
+ * sfa_decode -- sparse MLA attention over the selected latent rows: each
+ * query head attends only to the rows of its token's index row, through the
+ * one 576-wide latent row MLA keeps per position, keys the whole row and
+ * values its first 512 elements ("Day0 Inference Adaptation and Performance
+ * Optimization for a Sparse Hybrid Architecture LLM", sec. 1 and 2.1; FP8
+ * cache layouts: "Optimizing Inference for Hybrid Attention LLMs", sec. 4
+ * table; "Day-0 Inference Adaptation and Optimization for Hybrid Attention
+ * Architectures", sec. 4).
  *
  *   q          [T,H,576] bf16 query (latent-absorbed 512 + rope 64), H in {16,32,64,128}
  *   kv_cache   [num_pages,64,576] latent pool; LI_BF16 bits, or LI_FP8 codes with
@@ -193,9 +219,13 @@ li_status sfa_decode(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_len
                      size_t workspace_bytes, void* stream);
 
 /*
- * sfa_prefill -- the same operation for a prefill chunk (many query tokens of
- * one request, each with its own index row); same arguments and layouts as
- * sfa_decode.  It picks a launch shaped for many tokens (no index-list split).
+ * sfa_prefill -- the same operation for a prefill chunk (many query tokens
+ * per request, each with its own causal index row: "Day0 Inference Adaptation
+ * and Performance Optimization for a Sparse Hybrid Architecture LLM", sec. 2.1
+ * -- prefill and decode attention over the selected rows); same arguments,
+ * layouts and results as sfa_decode, and the same kernels and launch choice:
+ * the split of a token's index row over workgroups follows from the token
+ * count, so a chunk of many tokens runs unsplit.
  */
 li_status sfa_prefill(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                       int32_t max_pages, int32_t num_pages, const void* q, int32_t num_heads, int32_t kv_dtype,
@@ -230,12 +260,13 @@ size_t li_decode_step_workspace_size(int32_t num_seqs, int32_t q_per_seq, int32_
  * One launch for bf16 query, keys and latent, q_per_seq = 1, num_heads = 128
  * and at most one 4096-position chunk per compute unit (num_seqs *
  * ceil(max_pages * 64 / 4096) <= CUs, <= 64 chunks per request): each
- * chunk's workgroup scores its chunk, writes its share of the index row, then
- * runs attention splits of its request once the row is complete and merges
- * the split partials in the same launch.  Other shapes run li_score_topk and
- * sfa_decode back to back.  idx_out is identical to li_score_topk's; out and
- * lse equal sfa_decode's up to the rounding of the split partials (the
- * fused launch splits the index row differently).
+ * chunk's workgroup scores its chunk, writes its share of the index row,
+ * attends to the selected positions that lie in its chunk (one partial per
+ * chunk), and the request's workgroups merge the partials once every chunk
+ * has published its own, in the same launch.  Other shapes run li_score_topk
+ * and sfa_decode back to back.  idx_out is identical to li_score_topk's; out
+ * and lse equal sfa_decode's up to the rounding of the partials (the fused
+ * launch splits the index row by chunk, not by rank).
  */
 li_status li_decode_step(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
                          int32_t max_pages, int32_t num_pages, int32_t q_dtype, const void* q_idx,

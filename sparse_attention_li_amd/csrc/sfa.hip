@@ -30,9 +30,9 @@
 //     P^T comes straight from the S^T registers (the MFMA k-slot order is
 //     chosen to match the S^T output layout) and C^T is read from the LDS tile
 //     with the gfx950 transpose read ds_read_b64_tr_b16.
-// When a token's index row is split over several workgroups, each writes an
-// unnormalised fp32 partial and (max, sum) per head, and a combine kernel
-// merges them.
+// When a token's index row is split over several workgroups, each writes its
+// output normalised by its own sum (bf16) and (max in log2 units, sum) per
+// head, and a combine kernel merges them.
 #include "sfa_bf16_body.h"
 
 namespace sli {
