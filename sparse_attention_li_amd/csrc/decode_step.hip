@@ -16,8 +16,8 @@
 //      selection that lie in its chunk, so no workgroup waits for another's
 //      index writes -- giving a partial (max, sum, normalised output) per head;
 //   3. once every chunk of the request has published its partial (a count),
-//      merge items of 16 heads, taken from a counter by the request's
-//      workgroups, combine the partials into the output and lse.
+//      the request's workgroups combine the partials into the output and lse,
+//      in items of 16 heads dealt by arrival order at the count.
 // A request of one chunk writes its output in step 2.  When the indexer's
 // exchanges fell back (a workgroup gave up and the last one to arrive wrote
 // the whole request), that last workgroup attends over the whole selection
@@ -35,11 +35,14 @@ constexpr int kStepRing = 4;      // key tiles in flight per wave
 constexpr int kStepRows = 2048;   // pool rows one workgroup attends, at most (top_k)
 constexpr int kStepMergeHeads = 16;  // heads per merge item: 16 threads per head
 static_assert(kStepMergeHeads * 16 == kStepWaves * 64, "one merge item per workgroup pass");
+constexpr int kStepHeads = 128;      // query heads of the step: 8 merge items, 8 "gave up" bits
+static_assert(kStepHeads / kStepMergeHeads <= 16, "one gave-up bit per item owner in the upper half-word");
 
-// Per-request words of the step (the request's counter line; words 0..2
-// belong to the indexer's exchanges).  The launch's last workgroup to depart
-// zeroes them.
-enum : uint32_t { kStAttnDone = 4, kStMerge = 5 };
+// Per-request word of the step (in the request's counter line; words 0..2
+// belong to the indexer's exchanges): the count of published partials in the
+// low 16 bits, and from bit 16 one "gave up" bit per arrival order that owns
+// merge items.  The launch's last workgroup to depart zeroes it.
+enum : uint32_t { kStAttn = 4 };
 
 typedef IdxSmem<1, kStepWaves, kStepChunk, false, kStepRing> StepIdxSmem;
 
@@ -67,45 +70,42 @@ struct StepSmall {
 };
 static_assert(kStepX + sizeof(StepSmall) <= 160 * 1024, "LDS of one CU");
 
-// Polls the counter at p until it reaches `target` (bounded).
-__device__ __forceinline__ bool poll_at_least(const uint32_t* p, uint32_t target, int spin_max) {
-  for (int spins = 0;; ++spins) {
-    if (xload(p) >= target) return true;
-    if (spins >= spin_max) return false;
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-// Thread 0 adds 1 to the counter at p (device scope) once everything the
-// workgroup wrote is complete in memory; every thread receives whether the
-// count reached `target` with it.
-__device__ __forceinline__ bool count_and_check(uint32_t* p, uint32_t target, uint32_t* bc) {
+// Thread 0 adds 1 to the count of the word at p (device scope) once
+// everything the workgroup wrote is complete in memory; every thread receives
+// the word as it was before.
+__device__ __forceinline__ uint32_t count_in(uint32_t* p, uint32_t* bc) {
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bc[0] = old + 1u >= target ? 1u : 0u;
-  }
-  __syncthreads();
-  const bool r = bc[0] != 0u;
-  __syncthreads();
-  return r;
-}
-
-// Thread 0 polls; every thread receives the outcome.
-__device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target, int spin_max, uint32_t* bc) {
-  if (threadIdx.x == 0) bc[0] = poll_at_least(p, target, spin_max) ? 1u : 0u;
-  __syncthreads();
-  const bool r = bc[0] != 0u;
-  __syncthreads();
-  return r;
-}
-
-// Thread 0 takes the next item of the counter at p; every thread receives it.
-__device__ __forceinline__ uint32_t take_item(uint32_t* p, uint32_t* bc) {
   if (threadIdx.x == 0) bc[0] = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t r = bc[0];
+  __syncthreads();
+  return r;
+}
+
+// Thread 0 polls the count of the word at p until it reaches `target`
+// (bounded); on time-out it sets the "gave up" bit `bit` and learns from the
+// same atomic whether the count completed meanwhile.  Every thread receives
+// whether the count is complete (the partials are all in memory).
+__device__ __forceinline__ bool wait_count(uint32_t* p, uint32_t target, uint32_t bit, int spin_max, uint32_t* bc) {
+  if (threadIdx.x == 0) {
+    bool done = false;
+    for (int spins = 0;; ++spins) {
+      if ((xload(p) & 0xffffu) >= target) {
+        done = true;
+        break;
+      }
+      if (spins >= spin_max) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (!done) {
+      const uint32_t w = __hip_atomic_fetch_or(p, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      done = (w & 0xffffu) >= target;  // the last arrived before the bit: it did not see it
+    }
+    bc[0] = done ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool r = bc[0] != 0u;
   __syncthreads();
   return r;
 }
@@ -140,17 +140,31 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
                          reinterpret_cast<char*>(X + 2 * kTileBytes), reinterpret_cast<char*>(X + 3 * kTileBytes),
                          Z.att.pbuf, Z.att.rows};
     sfa_bf16_body<kStepWaves, kStepRows, true>(s.att, lds, b, c, n_own, direct);
-    // 3. merge, once every chunk's partial is out
+    // 3. merge, once every chunk's partial is out.  The workgroup of arrival
+    // order o at the count merges items o, o + n_chunks, ...  One that gives
+    // up waiting sets its bit: the last to arrive then merges its items too,
+    // unless the count completed before the bit was set, when it merges them
+    // itself (exactly one of the two sees the other).  When the count never
+    // completes (an exchange fell back and one workgroup wrote the whole
+    // request, attending over all of it), every waiter gives up.
     if (!direct) {
-      const bool last = count_and_check(&rl[kStAttnDone], n_chunks, bc);
-      bool merge = last || wait_at_least(&rl[kStAttnDone], n_chunks, a.spin_max, bc);
       const uint32_t n_items = (uint32_t)((s.att.H + kStepMergeHeads - 1) / kStepMergeHeads);
-      while (merge) {
-        const uint32_t m = take_item(&rl[kStMerge], bc);
-        if (m >= n_items) break;
-        // 16 threads per head, 32 columns each: every load of a split group in flight at once
-        const int h = (int)m * kStepMergeHeads + (int)(threadIdx.x >> 4);
-        if (h < s.att.H) sfa_merge_head<true, 4>(s.att, b, h, threadIdx.x & 15, (int)n_chunks);
+      const uint32_t old = count_in(&rl[kStAttn], bc);
+      const uint32_t o = old & 0xffffu;
+      const bool last = o + 1u == n_chunks;
+      auto merge_items = [&](uint32_t owner) {
+        for (uint32_t m = owner; m < n_items; m += n_chunks) {
+          // 16 threads per head, 32 columns each: every load of a split group in flight at once
+          const int h = (int)m * kStepMergeHeads + (int)(threadIdx.x >> 4);
+          if (h < s.att.H) sfa_merge_head<true, 4>(s.att, b, h, threadIdx.x & 15, (int)n_chunks);
+        }
+      };
+      if (last) {
+        merge_items(o);
+        for (uint32_t g = 0; g < o && g < n_items; ++g)
+          if ((old >> (16 + g)) & 1u) merge_items(g);
+      } else if (o < n_items && wait_count(&rl[kStAttn], n_chunks, 1u << (16 + o), a.spin_max, bc)) {
+        merge_items(o);
       }
     }
   }
@@ -164,11 +178,9 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
   }
   __syncthreads();
   if (bc[1]) {
-    for (int r = threadIdx.x; r < a.B; r += blockDim.x) {
-      uint32_t* rl = a.counters + (size_t)r * kCounterStride;
-      __hip_atomic_store(&rl[kStAttnDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&rl[kStMerge], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int r = threadIdx.x; r < a.B; r += blockDim.x)
+      __hip_atomic_store(&a.counters[(size_t)r * kCounterStride + kStAttn], 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) {
       __hip_atomic_store(&grid_line[kGridDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&grid_line[kGridEpoch], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
