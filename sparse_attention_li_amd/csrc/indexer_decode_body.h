@@ -321,10 +321,13 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
     return 1024 * (row / RPI) + 16 * ((64 / RPI) * (row % RPI) + 8 * (col >> 3) + ((col & 7) ^ (row & 7)));
   };
 
-  auto compute = [&](int tile, int slot_i) {
-    const int pos0 = s0 + tile * 32;
+  // Scoring a tile is split in two: the MFMAs (operand reads of the slot
+  // awaited inside, so the slot may be refilled right after), and the head
+  // sums of their results.  acc receives S[head, pos] of the tile's 32
+  // positions (two 32-head tiles per query token); ksw the FP8 row's scale
+  // word: its f32 scale, or (MXFP8 keys) its four E8M0 codes, group g in byte g.
+  auto scores = [&](int slot_i, f32x16 (&acc)[NQ * 2], uint32_t& ksw) {
     const unsigned char* src = ring + slot_i * SB;
-    f32x16 acc[NQ * 2];
 #pragma unroll
     for (int mt = 0; mt < NQ * 2; ++mt) acc[mt] = (f32x16){};
     // The operand reads of the ring are LDS instructions of their own, each
@@ -346,10 +349,8 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       SLI_KB_STEP(0) SLI_KB_STEP(1) SLI_KB_STEP(2) SLI_KB_STEP(3)
       SLI_KB_STEP(4) SLI_KB_STEP(5) SLI_KB_STEP(6) SLI_KB_STEP(7)
 #undef SLI_KB_STEP
+      ksw = 0u;
     }
-    // FP8 row n's scale word: its f32 scale, or (MXFP8 keys) its four E8M0
-    // codes, group g in byte g
-    uint32_t ksw = 0u;
     if constexpr (FP8) {
       // k-step j: row n, bytes 64 j + 16 half (chunk 4j + half) and 64 j + 32 + 16 half
       i32x4 kr[4];
@@ -373,20 +374,50 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
                                                                    qa[mt].scale[j], 0, kbs);
       }
     }
+  };
+  // Head weights of this lane's accumulator rows (rows 8g + 4 half + i of
+  // head tile mh): held in registers by the single-launch step, whose
+  // indexer phase has the registers of the attention phase to spare.
+  float wreg[FUSED ? NQ : 1][FUSED ? 32 : 1];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wreg[j][16 * mh + 4 * g + i] = sm.w[j][32 * mh + 8 * g + 4 * half + i];
+  }
+  // Weighted ReLU head sum of a tile's scores (four partial sums, added
+  // pairwise), its key into LDS and the lane's key range.
+  auto head_sums = [&](int tile, const f32x16 (&acc)[NQ * 2], uint32_t ksw) {
+    const int pos0 = s0 + tile * 32;
     const float kscale = (FP8 && !a.k_mx) ? __uint_as_float(ksw) : 1.f;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      float part = 0.f;
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mh = 0; mh < 2; ++mh) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           // output rows 8g+4*half+0..3 of this 32-head tile: four consecutive heads
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(&sm.w[j][32 * mh + 8 * g + 4 * half]);
+          f32x4 w4;
+          if constexpr (FUSED) {
+            w4 = (f32x4){wreg[j][16 * mh + 4 * g], wreg[j][16 * mh + 4 * g + 1], wreg[j][16 * mh + 4 * g + 2],
+                         wreg[j][16 * mh + 4 * g + 3]};
+          } else {
+            w4 = *reinterpret_cast<const f32x4*>(&sm.w[j][32 * mh + 8 * g + 4 * half]);
+          }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += w4[i] * fmaxf(acc[2 * j + mh][4 * g + i], 0.f);
+          for (int i = 0; i < 4; ++i) {
+            // bf16: four partial sums, as the single-launch step's scorer adds them
+            if constexpr (FP8) p4[0] += w4[i] * fmaxf(acc[2 * j + mh][4 * g + i], 0.f);
+            else p4[i] += w4[i] * fmaxf(acc[2 * j + mh][4 * g + i], 0.f);
+          }
         }
       }
+      float part = FP8 ? p4[0] : (p4[0] + p4[1]) + (p4[2] + p4[3]);
       part += __shfl_xor(part, 32, kWave);
       if constexpr (FP8) part *= kscale;  // positive per-row scale commutes with ReLU (1 for MXFP8 keys)
       if (half == 0) {
@@ -410,7 +441,65 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
   // Slots are consumed in ring order; the tile dealt next refills the slot
   // just consumed.  Tiles are dealt in increasing order, so the first slot
   // found without a tile ends the loop.
+  // The single-launch step (bf16, one query token, one wave per SIMD): the
+  // MFMAs of one tile with the head sums of the previous tile interleaved,
+  // a quarter of a 32-head block per k-step, so the wave's vector work is
+  // issued while its matrix work runs (in-order issue would otherwise hold
+  // the head sums behind the last MFMA of the tile).
+  auto scores_overlap = [&](int slot_i, f32x16 (&acc)[NQ * 2], const f32x16 (&prev)[NQ * 2], int prev_tile,
+                            bool has_prev) {
+    if constexpr (!FP8 && NQ == 1 && FUSED) {
+    const unsigned char* src = ring + slot_i * SB;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = (f32x16){};
+    const uint32_t src_a = (uint32_t)(size_t)(const lds_void*)src;
+    bf16x8 kb[8];
+#define SLI_KB_READ(J) asm volatile("ds_read_b128 %0, %1" : "=v"(kb[J]) : "v"(src_a + (uint32_t)slot(n, 8 * half + J)));
+    SLI_KB_READ(0) SLI_KB_READ(1) SLI_KB_READ(2) SLI_KB_READ(3)
+    SLI_KB_READ(4) SLI_KB_READ(5) SLI_KB_READ(6) SLI_KB_READ(7)
+#undef SLI_KB_READ
+    float p4[4] = {0.f, 0.f, 0.f, 0.f};
+    // k-step J: the MFMAs of this tile, then the previous tile's heads of
+    // block J / 4, rows 8 (J % 4) + 4 half + 0..3
+#define SLI_KB_STEP_OV(J)                                                                                  \
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kb[J]) : "i"(7 - J));                                       \
+  acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0].v[J], kb[J], acc[0], 0, 0, 0);                 \
+  acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1].v[J], kb[J], acc[1], 0, 0, 0);                 \
+  if (has_prev) {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
+      p4[i] += wreg[0][4 * (J) + i] * fmaxf(prev[(J) >> 2][4 * ((J) & 3) + i], 0.f);                    \
+  }                                                                                                       \
+  __builtin_amdgcn_sched_barrier(0);
+    SLI_KB_STEP_OV(0) SLI_KB_STEP_OV(1) SLI_KB_STEP_OV(2) SLI_KB_STEP_OV(3)
+    SLI_KB_STEP_OV(4) SLI_KB_STEP_OV(5) SLI_KB_STEP_OV(6) SLI_KB_STEP_OV(7)
+#undef SLI_KB_STEP_OV
+    if (has_prev) {
+      float part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      part += __shfl_xor(part, 32, kWave);
+      if (half == 0) {
+        const int s = s0 + prev_tile * 32 + n;
+        const uint32_t key = (s < vis[0]) ? score_key(part) : 0u;
+        const uint32_t ka = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)&s_keys[prev_tile * 32 + n];
+        asm volatile("ds_write_b32 %0, %1" : : "v"(ka), "v"(key) : "memory");
+        if (key != 0u) {
+          kmin[0] = min(kmin[0], key);
+          kmax[0] = max(kmax[0], key);
+        }
+      }
+    }
+    }
+  };
+
   bool more = tq[0] < nt_used;
+  // The single-launch step runs one wave per SIMD, so the head sums of each
+  // tile wait for the next tile's MFMAs to be issued (accumulator sets
+  // alternating with the slot parity); with two waves per SIMD the other
+  // wave fills those gaps and each tile is finished in turn.
+  constexpr bool kOverlap = FUSED;
+  static_assert(!kOverlap || RS % 2 == 0, "accumulator sets alternate with the slot parity");
+  f32x16 acc0[NQ * 2], acc1[NQ * 2];
+  uint32_t ksw0 = 0u, ksw1 = 0u;
+  int tile0 = 0, tile1 = 0, pend = -1;  // pend: the set whose head sums are outstanding
 #pragma unroll 1
   while (more) {
 #pragma unroll
@@ -434,7 +523,22 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
 #undef SLI_WAIT_CASE
         default: SLI_WAIT_VMCNT(0); break;
       }
-      compute(tq[s], s);
+      const int tile = tq[s];
+      if constexpr (kOverlap) {
+        // this tile into the set of the slot parity, the previous one's head sums beside its MFMAs
+        if ((s & 1) == 0) {
+          scores_overlap(s, acc0, acc1, tile1, pend == 1);
+          tile0 = tile;
+          pend = 0;
+        } else {
+          scores_overlap(s, acc1, acc0, tile0, pend == 0);
+          tile1 = tile;
+          pend = 1;
+        }
+      } else {
+        scores(s, acc0, ksw0);
+        head_sums(tile, acc0, ksw0);
+      }
       int g = nt_used;
       if (pre < nt_used) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this slot's operand reads are done
@@ -445,6 +549,8 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       pre = g;
     }
   }
+  if (pend == 0) head_sums(tile0, acc0, ksw0);
+  if (pend == 1) head_sums(tile1, acc1, ksw1);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const uint32_t mn = wave_min(kmin[j]), mx = wave_max(kmax[j]);
