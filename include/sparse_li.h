@@ -277,6 +277,23 @@ li_status li_decode_step(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq
                          size_t workspace_bytes, void* stream);
 
 /*
+ * li_validate_paged -- checks the paged-cache metadata on the device (debug
+ * aid; no kernel depends on it).  The conventions above require block-table
+ * entries in [0, num_pages) and 0 <= L_b <= max_pages*64; the kernels clamp
+ * violations, so a bad table gives wrong results rather than an access
+ * outside the pools, and this call finds them.  Library housekeeping: no
+ * passage of the pages defines it.
+ *   seq_lens     [num_seqs] int32, block_table [num_seqs, max_pages] int32 (device)
+ *   bad_out      one int32 (device, 4-byte aligned): set to the number of
+ *                requests whose length lies outside [0, max_pages*64] plus the
+ *                number of pages in use (p < ceil(L_b/64), L_b held to that
+ *                range) whose id lies outside [0, num_pages)
+ * Asynchronous on `stream` (a fill kernel clears bad_out first; no memset).
+ */
+li_status li_validate_paged(int32_t num_seqs, const int32_t* seq_lens, const int32_t* block_table, int32_t max_pages,
+                            int32_t num_pages, int32_t* bad_out, void* stream);
+
+/*
  * li_quantize_mxfp8 -- MXFP8 quantisation of bf16 rows, e.g. the indexer
  * query before li_score_topk ("Day-0 Inference Adaptation and Optimization
  * for Hybrid Attention Architectures", sec. 4: MXFP8 indexer query, group 32;

@@ -19,7 +19,7 @@ import torch
 __all__ = ["li_score_topk", "sfa_decode", "sfa_prefill", "lib", "LI_BF16", "LI_FP8", "LI_MXFP8", "LI_FP8_ROPE_BF16", "LiError",
            "li_score_topk_workspace_size", "sfa_workspace_size", "li_workspace_zero", "li_quantize_mxfp8",
            "li_set_exchange_patience", "li_score_topk_noalloc", "li_decode_step", "li_decode_step_workspace_size",
-           "li_cache_append"]
+           "li_cache_append", "li_validate_paged"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_li.so")
@@ -30,7 +30,8 @@ _STATUS = {-1: "LI_ERR_INVALID_ARG", -2: "LI_ERR_UNSUPPORTED", -3: "LI_ERR_WORKS
 
 EXPORTS = ["li_version", "li_last_error", "li_set_exchange_patience", "li_score_topk_workspace_size",
            "li_score_topk_noalloc", "li_decode_step", "li_decode_step_workspace_size", "li_workspace_zero", "li_score_topk",
-           "sfa_workspace_size", "sfa_decode", "sfa_prefill", "li_quantize_mxfp8", "li_cache_append"]
+           "sfa_workspace_size", "sfa_decode", "sfa_prefill", "li_quantize_mxfp8", "li_cache_append",
+           "li_validate_paged"]
 
 
 class LiError(RuntimeError):
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.li_score_topk_workspace_size.argtypes = [i32, i32, i32, i32]
         L.li_workspace_zero.restype = i32
         L.li_workspace_zero.argtypes = [vp, sz, vp]
+        L.li_validate_paged.restype = i32
+        L.li_validate_paged.argtypes = [i32, vp, vp, i32, i32, vp, vp]
         L.li_score_topk.restype = i32
         L.li_score_topk.argtypes = [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp, sz, vp]
         L.li_score_topk_noalloc.restype = i32
@@ -122,6 +125,18 @@ def li_set_exchange_patience(polls: int):
 
 def li_workspace_zero(ws: torch.Tensor, stream=None):
     _check(lib().li_workspace_zero(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def li_validate_paged(seq_lens: torch.Tensor, block_table: torch.Tensor, num_pages: int, stream=None) -> torch.Tensor:
+    """Device-side check of the paged-cache metadata: returns a one-element
+    int32 device tensor with the number of problems found (requests whose
+    length lies outside [0, max_pages*64], used pages whose id lies outside
+    [0, num_pages))."""
+    B, max_pages = block_table.shape
+    bad = torch.empty(1, dtype=torch.int32, device=block_table.device)
+    _check(lib().li_validate_paged(B, _ptr(seq_lens), _ptr(block_table), max_pages, num_pages, _ptr(bad),
+                                   _stream(stream)))
+    return bad
 
 
 _ws_cache: dict = {}

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_li.so")
 
 SOURCES = ["abi.cpp", "shapes.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "quant.hip", "noalloc.hip",
-           "decode_step.hip"]
+           "decode_step.hip", "validate.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

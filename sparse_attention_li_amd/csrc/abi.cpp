@@ -490,6 +490,25 @@ li_status li_decode_step(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq
   return e == hipSuccess ? LI_OK : hip_fail(e, "decode step launch");
 }
 
+li_status li_validate_paged(int32_t num_seqs, const int32_t* seq_lens, const int32_t* block_table, int32_t max_pages,
+                            int32_t num_pages, int32_t* bad_out, void* stream) {
+  if (num_seqs <= 0 || max_pages <= 0 || num_pages <= 0)
+    return fail(LI_ERR_INVALID_ARG, "num_seqs, max_pages and num_pages must be positive (got %d, %d, %d)", num_seqs,
+                max_pages, num_pages);
+  if (!seq_lens || !block_table || !bad_out)
+    return fail(LI_ERR_INVALID_ARG, "seq_lens, block_table and bad_out must not be NULL");
+  if (reinterpret_cast<uintptr_t>(bad_out) & 3u) return fail(LI_ERR_INVALID_ARG, "bad_out must be 4-byte aligned");
+  sli::ValidateArgs a;
+  a.B = num_seqs;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.bad_out = bad_out;
+  hipError_t e = sli::launch_validate_paged(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LI_OK : hip_fail(e, "validation launch");
+}
+
 li_status li_quantize_mxfp8(int32_t n_rows, int32_t row_len, const void* x, uint8_t* codes, uint8_t* scales,
                             void* stream) {
   if (n_rows < 0) return fail(LI_ERR_INVALID_ARG, "n_rows must not be negative (got %d)", n_rows);

@@ -94,6 +94,13 @@ struct AppendArgs {
   float* kv_scales;   // [num_pages][64][kv_groups] (FP8)
 };
 
+struct ValidateArgs {
+  int B, max_pages, num_pages;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t* bad_out;  // one int32: the count of problems found
+};
+
 // Records a failure message for li_last_error() (printf format) and returns s.
 li_status report(li_status s, const char* fmt, ...);
 
@@ -107,6 +114,7 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_decode_step(const StepArgs& s, hipStream_t stream);
+hipError_t launch_validate_paged(const ValidateArgs& a, hipStream_t stream);
 int sfa_heads_per_block(int H, bool fp8);
 
 }  // namespace sli

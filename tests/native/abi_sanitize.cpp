@@ -282,6 +282,18 @@ int main() {
   step_case(4, 1, LI_BF16, 64, 512, 2048, "idx_decode sfa ");
 
   quant_and_append();
+  {
+    Batch b(5, 7, 300);
+    Buf bad(4);
+    g_stub.calls.clear();
+    CHECK(li_validate_paged(b.B, b.lens.data(), b.bt.data(), b.max_pages, b.num_pages, bad.as<int32_t>(), nullptr) ==
+          LI_OK);
+    CHECK(g_stub.calls == "validate ");
+    CHECK(li_validate_paged(0, b.lens.data(), b.bt.data(), b.max_pages, b.num_pages, bad.as<int32_t>(), nullptr) ==
+          LI_ERR_INVALID_ARG);
+    CHECK(li_validate_paged(b.B, b.lens.data(), b.bt.data(), b.max_pages, b.num_pages, nullptr, nullptr) ==
+          LI_ERR_INVALID_ARG);
+  }
   errors();
   if (failures) {
     fprintf(stderr, "%d checks failed\n", failures);

@@ -139,6 +139,13 @@ hipError_t launch_decode_step(const StepArgs& s, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_validate_paged(const ValidateArgs& a, hipStream_t) {
+  g_stub.calls += "validate ";
+  seqs(a.seq_lens, a.block_table, a.B, a.max_pages);
+  wr(a.bad_out, 4, "bad_out");
+  return hipSuccess;
+}
+
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t) {
   g_stub.calls += "zero ";
   wr(p, bytes, "zero_fill");

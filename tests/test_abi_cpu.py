@@ -140,3 +140,13 @@ def test_noalloc_rejects_geometries_beyond_its_array():
     assert st == -2 and b"li_score_topk_noalloc" in L.li_last_error()
     st = L.li_score_topk_noalloc(0, 1, P, P, 32, 32, 0, P, None, P, 0, P, None, 256, P, None)
     assert st == -1 and L.li_last_error()
+
+
+def test_validate_paged_argument_errors():
+    L = li.lib()
+    P = ctypes.c_void_p(0x10000)
+    assert L.li_validate_paged(0, P, P, 4, 8, P, None) == -1
+    assert L.li_validate_paged(2, None, P, 4, 8, P, None) == -1
+    assert L.li_validate_paged(2, P, P, 4, 0, P, None) == -1
+    assert L.li_validate_paged(2, P, P, 4, 8, ctypes.c_void_p(0x10002), None) == -1
+    assert L.li_last_error()

@@ -131,3 +131,40 @@ def test_cache_append_matches_oracle(li, fp8_k, fp8_kv, groups, n_q):
             continue
         g = got.cpu().numpy()
         assert np.array_equal(g.view(np.uint8), want.view(np.uint8)), f"{name}: {int((g != want).sum())} mismatches"
+
+
+def _bad_metadata_count(seq_lens, bt, num_pages):
+    """Host count of what li_validate_paged reports, from its documented rule."""
+    B, max_pages = bt.shape
+    cap = max_pages * 64
+    bad = 0
+    for b in range(B):
+        L = int(seq_lens[b])
+        bad += int(L < 0 or L > cap)
+        used = (min(max(L, 0), cap) + 63) // 64
+        bad += int(((bt[b, :used] < 0) | (bt[b, :used] >= num_pages)).sum())
+    return bad
+
+
+def test_validate_paged_counts_bad_metadata(li):
+    """The device check of the paged-cache metadata: a valid table gives 0; a
+    table with planted bad lengths and page ids (some on unused pages, which
+    do not count) gives the host count."""
+    rng = np.random.default_rng(71)
+    B, max_pages, num_pages = 6, 10, 40
+    lens = np.array([0, 64, 65, 640, 641, -3], np.int32)
+    bt = rng.integers(0, num_pages, (B, max_pages)).astype(np.int32)
+    dev = lambda x: torch.from_numpy(x).cuda()
+    ok_lens = np.clip(lens, 0, 640).astype(np.int32)
+    assert int(li.li_validate_paged(dev(ok_lens), dev(bt), num_pages).item()) == 0
+    bt[0, 0] = -5           # request of length 0: page unused
+    bt[1, 0] = -1           # used
+    bt[2, 1] = num_pages    # used (65 positions: pages 0 and 1)
+    bt[2, 5] = -1           # unused
+    bt[3, 9] = 1000         # used (640 positions: all ten pages)
+    bt[4, 2] = -2           # used (641 is held to 640)
+    want = _bad_metadata_count(lens, bt, num_pages)
+    assert want == 6
+    assert int(li.li_validate_paged(dev(lens), dev(bt), num_pages).item()) == want
+    # a second call on the same output clears it first
+    assert int(li.li_validate_paged(dev(ok_lens), dev(bt), num_pages).item()) == _bad_metadata_count(ok_lens, bt, num_pages)
