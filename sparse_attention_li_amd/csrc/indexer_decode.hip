@@ -47,9 +47,6 @@ hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStr
     // streams while the other selects (eight-wave ones fill a CU alone)
     if (fp8 && a.xcd_local)
       return a.n_q == 1 ? launch_one<1, 4, 4096, true>(a, stream) : launch_one<2, 4, 4096, true>(a, stream);
-#ifdef SLI_PROBE_W4R4
-    if (a.n_q == 1 && !fp8) return launch_one<1, 4, 4096, false, 4>(a, stream);
-#endif
     if (a.n_q == 1) return fp8 ? launch_one<1, 8, 4096, true>(a, stream) : launch_one<1, 8, 4096, false>(a, stream);
     if (a.n_q == 2 && fp8) return launch_one<2, 8, 4096, true>(a, stream);
   }

@@ -81,13 +81,9 @@ __host__ __device__ constexpr bool sfa_pv_schedule_ok(int ahead) {
 constexpr int kPvAhead = 1;  // transposed pairs read ahead of their first MFMA
 static_assert(sfa_pv_schedule_ok(1) && sfa_pv_schedule_ok(2), "output-product read schedule");
 
-#ifndef SLI_NO_PINS
+// keep a value in a vector / an accumulation register across the statement
 #define SLI_PIN_V(x) asm volatile("" : "+v"(x))
 #define SLI_PIN_A(x) asm volatile("" : "+a"(x))
-#else
-#define SLI_PIN_V(x)
-#define SLI_PIN_A(x)
-#endif
 // LDS of the all-heads body: four ring slots of one tile each (the targets
 // of the direct-to-LDS gathers; no C++ access may touch a slot while loads
 // into any slot are in flight), the weights buffer and the slice's row ids.
