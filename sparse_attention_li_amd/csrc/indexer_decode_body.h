@@ -50,7 +50,7 @@
 namespace sli {
 
 constexpr int kHistBins = 4096;  // LDS histogram that brackets a chunk's R-th largest key
-constexpr int kBandCap = 4096;   // band entries the final select keeps in LDS
+constexpr int kBandCap = 3584;   // band entries the final select keeps in LDS (a multiple of 512)
 
 // Words of the fixed counter region (one 128-byte line per request, then one
 // line for the whole launch).  Exchange data carries a per-call tag (the
@@ -73,14 +73,13 @@ struct IdxSmem {
   static constexpr int kTileBytes = FP8 ? 32 * 128 : 32 * 256;
   static constexpr int kSlotBytes = kTileBytes + (FP8 ? 128 : 0);  // FP8: the tile's 32 row scales follow it
   static constexpr int kRing = NW * RS * kSlotBytes;
-  static constexpr int kReuse = kBandCap * 8 > kHistBins * 4 ? kBandCap * 8 : kHistBins * 4;
+  // after scoring: the band entries, then the per-chunk offsets and the
+  // whole-request writer's bitmap (kSel bytes), or the histogram
+  static constexpr int kSel = kBandCap * 8 + (3 * kMaxChunksPerSeq + 2) * 4 + CHUNK / 8;
+  static constexpr int kReuse = kSel > kHistBins * 4 ? kSel : kHistBins * 4;
   static constexpr int kArena = kRing > kReuse ? kRing : kReuse;
   alignas(16) float w[NQ][64];
   uint32_t hist[256];                    // radix-select digits
-  uint32_t cbase[kMaxChunksPerSeq + 1];  // band entries before each chunk
-  uint32_t abase[kMaxChunksPerSeq + 1];  // keys >= hi before each chunk
-  uint32_t nabove[kMaxChunksPerSeq];     // keys >= hi per chunk
-  uint32_t bitmap[CHUNK / 32];           // selected positions of one chunk (whole-request writer)
   uint32_t mm[NQ][NW][2];                // per-wave min / max valid key
   uint32_t ref[NQ][2];                   // [lo, hi) of this chunk
   uint32_t sel[4];
@@ -794,6 +793,13 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
   // 3. exact select among the band entries, then the writes
   uint32_t* s_bk = reinterpret_cast<uint32_t*>(lds.arena);       // [kBandCap] band keys
   int32_t* s_bp = reinterpret_cast<int32_t*>(s_bk + kBandCap);  // [kBandCap] their positions
+  // (in the arena after the band: the key ring is dead, and sharing it lets
+  // the four-wave FP8 workgroups fit three to a CU)
+  uint32_t* const cbase = reinterpret_cast<uint32_t*>(s_bp + kBandCap);  // [max chunks + 1] band entries before each chunk
+  uint32_t* const abase = cbase + kMaxChunksPerSeq + 1;                  // [max chunks + 1] keys >= hi before each chunk
+  uint32_t* const nabove = abase + kMaxChunksPerSeq + 1;                 // [max chunks] keys >= hi per chunk
+  uint32_t* const bitmap = nabove + kMaxChunksPerSeq;                    // [CHUNK / 32] one chunk's selected positions
+  static_assert(IdxSmem<NQ, NW, CHUNK, FP8, RS>::kSel <= IdxSmem<NQ, NW, CHUNK, FP8, RS>::kArena, "arena layout");
 #pragma unroll 1
   for (int j = 0; j < NQ; ++j) {
     if (vis[j] <= K) continue;
@@ -806,13 +812,13 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
     uint32_t cpre[2], ctot[2];
     block_excl_scan_n<2>(cv, sm.scan, cpre, ctot);
     if (tid < n_chunks) {
-      sm.abase[tid] = cpre[0];
-      sm.cbase[tid] = cpre[1];
-      sm.nabove[tid] = cv[0];
+      abase[tid] = cpre[0];
+      cbase[tid] = cpre[1];
+      nabove[tid] = cv[0];
     }
     if (tid == 0) {
-      sm.abase[n_chunks] = ctot[0];
-      sm.cbase[n_chunks] = ctot[1];
+      abase[n_chunks] = ctot[0];
+      cbase[n_chunks] = ctot[1];
     }
     __syncthreads();
     const uint32_t A = ctot[0], NB = ctot[1];
@@ -824,7 +830,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       int lo = 0, hi = n_chunks;  // cbase[lo] <= f < cbase[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if ((int)sm.cbase[mid] <= f) lo = mid; else hi = mid;
+        if ((int)cbase[mid] <= f) lo = mid; else hi = mid;
       }
       return lo;
     };
@@ -841,7 +847,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
           ev[r] = 0ull;
           if (f < (int)NB) {
             const int i = chunk_of(f);
-            ev[r] = xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
+            ev[r] = xload64(&a.cand[gaddr(i, f - cbase[i])]);
           }
         }
 #pragma unroll
@@ -858,7 +864,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
     auto key_at = [&](int f) -> uint32_t {
       if (in_lds) return s_bk[f];
       const int i = chunk_of(f);
-      return (uint32_t)xload64(&a.cand[gaddr(i, f - sm.cbase[i])]);
+      return (uint32_t)xload64(&a.cand[gaddr(i, f - cbase[i])]);
     };
     int ngt;
     uint32_t tau;
@@ -886,7 +892,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       // band entries before this chunk: how many are > tau, how many tie
       // (from global memory: eight reads per thread in flight)
       uint32_t gt = 0, eq = 0;
-      const int cb = (int)sm.cbase[c];
+      const int cb = (int)cbase[c];
       constexpr int LPT = 8;
 #pragma unroll 1
       for (int f0 = tid; f0 < cb; f0 += LPT * THREADS) {
@@ -919,7 +925,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       const uint32_t gt_before = stot[0], eq_before = stot[1], pre = spre[2];
       const uint32_t avail = ties > eq_before ? ties - eq_before : 0u;  // ties left for this chunk
       uint32_t tr = pre >> 16;                                            // ties of this chunk before my keys
-      const uint32_t o0 = sm.abase[c] + gt_before + min(ties, eq_before);  // this chunk's first output
+      const uint32_t o0 = abase[c] + gt_before + min(ties, eq_before);  // this chunk's first output
       uint32_t o = o0 + (pre & 0xffffu) + min(avail, tr);
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
@@ -938,14 +944,14 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       uint32_t off = 0, eq_seen = 0;
 #pragma unroll 1
       for (int i = 0; i < n_chunks; ++i) {
-        for (int wd = tid; wd < CHUNK / 32; wd += THREADS) sm.bitmap[wd] = 0u;
+        for (int wd = tid; wd < CHUNK / 32; wd += THREADS) bitmap[wd] = 0u;
         __syncthreads();
         const int ci0 = i * CHUNK;
-        for (uint32_t e = tid; e < sm.nabove[i]; e += THREADS) {
+        for (uint32_t e = tid; e < nabove[i]; e += THREADS) {
           const int pos = (int)(xload64(&a.cand[gaddr(i, CHUNK - 1 - e)]) >> 32);
-          atomicOr(&sm.bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
+          atomicOr(&bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
         }
-        const int f0 = (int)sm.cbase[i], f1 = (int)sm.cbase[i + 1];
+        const int f0 = (int)cbase[i], f1 = (int)cbase[i + 1];
 #pragma unroll 1
         for (int fb = f0; fb < f1; fb += THREADS) {
           const int f = fb + tid;
@@ -958,13 +964,13 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
           const uint32_t rank = eq_seen + block_excl_scan(tie ? 1u : 0u, sm.scan, et);
           if (f < f1 && (key > tau || (tie && rank < ties))) {
             const int pos = (int)(ev >> 32);
-            atomicOr(&sm.bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
+            atomicOr(&bitmap[(pos - ci0) >> 5], 1u << ((pos - ci0) & 31));
           }
           eq_seen += et;
         }
         __syncthreads();
         // emit in position order: thread t owns bits PER*t .. PER*t + PER-1
-        const uint32_t word = sm.bitmap[(PER * tid) >> 5];
+        const uint32_t word = bitmap[(PER * tid) >> 5];
         const uint32_t bits = (word >> ((PER * tid) & 31)) & ((1u << PER) - 1u);
         uint32_t et;
         uint32_t o = off + block_excl_scan((uint32_t)__popc(bits), sm.scan, et);
