@@ -42,6 +42,8 @@ hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStr
   } else if (chunk == 2048) {
     if (a.n_q == 1) return fp8 ? launch_one<1, 4, 2048, true>(a, stream) : launch_one<1, 4, 2048, false>(a, stream);
     if (a.n_q == 2) return fp8 ? launch_one<2, 4, 2048, true>(a, stream) : launch_one<2, 4, 2048, false>(a, stream);
+  } else if (chunk == 8192) {
+    if (fp8 && a.n_q == 1) return launch_one<1, 4, 8192, true>(a, stream);
   } else if (chunk == 4096) {
     // FP8 grids of several rounds: four-wave workgroups (56 / 72 KiB of LDS), two per CU, so one
     // streams while the other selects (eight-wave ones fill a CU alone)

@@ -6,12 +6,17 @@ namespace sli {
 
 // Positions per workgroup.  4096 (eight waves, one workgroup per CU) when
 // the grid still gives every CU a workgroup: each CU then streams the same
-// amount and the request's chunks finish together.  Smaller chunks (four
-// waves, two workgroups per CU) for small batches, and for bf16 two-token
-// calls, whose keys and key ring would not fit beside each other in LDS.
+// amount and the request's chunks finish together.  FP8 one-token grids that
+// would take more than one round of the chip at 4096 (three four-wave
+// workgroups per CU) use 8192: half the workgroups, so fewer requests wait at
+// their exchanges for chunks dispatched in a later round.  Smaller chunks
+// (four waves, two workgroups per CU) for small batches, and for bf16
+// two-token calls, whose keys and key ring would not fit beside each other in
+// LDS.
 int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus) {
   const long long maxlen = (long long)max_pages * 64;
   auto wgs = [&](long long ch) { return (long long)B * ((maxlen + ch - 1) / ch); };
+  if (fp8 && n_q == 1 && wgs(4096) > 3LL * cus) return 8192;
   if ((n_q == 1 || fp8) && wgs(4096) >= cus) return 4096;
   return wgs(1024) > 2LL * cus ? 2048 : 1024;
 }

@@ -85,6 +85,11 @@ SMALL = {
                                                            30001, 49152, 21000, 38000, 41000, 27000, 45000, 32768,
                                                            48000, 23000, 35000, 42000, 29000, 46000, 39000, 31000],
                           top_k=2048, H=16, idx_fmt="mxfp8", kv_fmt="fp8"),
+    # FP8 keys, one token, more than three workgroups per CU at 4096 positions: 8192-position chunks
+    "fp8_chunk8192": dict(seed=40, B=26, n_q=1, seq_lens=[131000, 90001, 8191, 8193, 16384, 1, 0, 300, 65536, 12345,
+                                                          7, 4096, 4097, 20000, 33, 50000, 8192, 100, 2, 24576, 1000,
+                                                          8000, 60000, 5, 30000, 129],
+                          top_k=2048, H=16, idx_fmt="fp8", kv_fmt="fp8"),
     # head weights of either sign: negative scores, ordered by their keys
     "signed_bf16": dict(seed=30, B=3, n_q=1, seq_lens=[900, 5000, 2049], top_k=512, H=32, signed_w=True),
     "signed_k_deep": dict(seed=31, B=2, n_q=1, seq_lens=[3000, 2500], top_k=2048, H=16, signed_w=True),
