@@ -119,17 +119,18 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
   uint32_t* const bc = reinterpret_cast<uint32_t*>(X);  // used between the phases only
 
   // 1. the indexer's chunk work; the rows of what this workgroup wrote
-  int b = 0, n_own = 0;
+  int b = 0, n_own = 0, n_chunks_b = 1;
   const int st = li_decode_body<1, kStepWaves, kStepChunk, false, kStepRing, true>(
       a, IdxLds<1, kStepWaves, kStepChunk, false, kStepRing>{Z.idx.sm, X, reinterpret_cast<uint32_t*>(X + StepIdxSmem::kArena),
                                                            Z.idx.pages},
-      tag, b, Z.att.rows, &n_own);
+      tag, b, Z.att.rows, &n_own, &n_chunks_b);
   __syncthreads();  // the indexer's LDS state is dead from here on; the rows are in place
 
   if (st == kBodyShare || st == kBodyAll) {
     uint32_t* rl = a.counters + (size_t)b * kCounterStride;
-    const int L = max(0, min(a.seq_lens[b], a.max_pages * 64));
-    const uint32_t n_chunks = (uint32_t)max(1, (L + kStepChunk - 1) / kStepChunk);
+    // (the count comes from the indexer: a reload of the length here would
+    // make every wave wait for all its stores in flight)
+    const uint32_t n_chunks = (uint32_t)n_chunks_b;
     const uint32_t ncm = (uint32_t)a.n_chunks_max;
     // the chunk of this workgroup, in the indexer's block layout
     const int c = a.xcd_local ? (int)((blockIdx.x >> 3) % ncm)

@@ -135,19 +135,21 @@ enum : int { kBodyNone = 0, kBodyShare = 1, kBodyAll = 2, kBodyQuit = 3 };
 
 // FUSED (the single-launch decode step): the key array lives in the same LDS
 // object as the key ring, so its stores are written as LDS instructions of
-// their own (a compiler store there would wait for every tile in flight), and
-// the index rows are written through to memory for workgroups on other XCDs
-// of the same launch.  Returns kBodyNone (no chunk of a request), kBodyShare
+// their own (a compiler store there would wait for every tile in flight).
+// Nothing in the launch reads the index rows (the attention takes the pool
+// rows from LDS), so they are ordinary stores, whose completion a later
+// memory wait does not have to await from HBM.  Returns kBodyNone (no chunk of a request), kBodyShare
 // (wrote this chunk's share of the rows), kBodyAll (wrote the whole request)
 // or kBodyQuit (left its share to the last workgroup); b_out = the request.
 // FUSED also records, in rows_out, the physical pool row of every position
 // the workgroup writes (its own selected positions, or the whole request's
 // when it writes the whole request), in output order, and their number in
-// n_own (every thread; at most top_k).
+// n_own (every thread; at most top_k), and the request's chunk count in
+// n_chunks_out (unless kBodyNone for padding past the last request).
 template <int NQ, int NW, int CHUNK, bool FP8, int RS, bool FUSED = false>
 __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ, NW, CHUNK, FP8, RS> lds,
                                               const uint32_t tag, int& b_out, int* rows_out = nullptr,
-                                              int* n_own = nullptr) {
+                                              int* n_own = nullptr, int* n_chunks_out = nullptr) {
   static_assert(!FUSED || NQ == 1, "the fused step takes one query token per request");
   IdxSmem<NQ, NW, CHUNK, FP8, RS>& sm = lds.sm;
   uint32_t* s_keys = lds.keys;  // [NQ][CHUNK]
@@ -223,6 +225,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
   uint32_t* ctr = a.counters + (size_t)b * kCounterStride;
   L = max(0, min(L, a.max_pages * 64));
   const int n_chunks = max(1, (L + CHUNK - 1) / CHUNK);
+  if constexpr (FUSED) *n_chunks_out = n_chunks;
   if (c >= n_chunks) return kBodyNone;
   if (tid < CHUNK / 64) lds.pages[tid] = (s0 + 64 * tid < L) ? min(max(pg, 0), a.num_pages - 1) : 0;
   if (tid < NQ * 64) sm.w[tid / 64][tid % 64] = wv;
@@ -564,10 +567,8 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
   // ---------------------------------------------------------------- selection
   const int K = a.top_k;
   const size_t ncm = (size_t)a.n_chunks_max;
-  // index-row stores: through to memory when other workgroups of the launch read them
-  auto put = [&](int32_t* p, int32_t v) {
-    if constexpr (FUSED) xstore(p, v); else *p = v;
-  };
+  // index-row stores (read only after the launch)
+  auto put = [&](int32_t* p, int32_t v) { *p = v; };
   // pool row of a position of this chunk (page ids in LDS) or of any
   // position of the request (block table)
   auto own_row = [&](int pos) { return lds.pages[(pos - s0) >> 6] * 64 + (pos & 63); };

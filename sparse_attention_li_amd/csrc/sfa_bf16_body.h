@@ -469,6 +469,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     char* const ld_dst = ring(ld_tile) + 1024 * wid_s;
     bf16x4 lo[8], hi[8];
     bf16x8 pv[2][4];
+    bf16x8 cv;  // the transposed pair of the current column tile, one operand
     if (do_pv) {
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) pp_issue(0, hb, pv[0][hb]);
@@ -482,8 +483,15 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
         if constexpr (hb == 0 && pi + kPvAhead < 8)
           pv_issue(c, (pi + kPvAhead) >> 2, (pi + kPvAhead) & 3, lo[pi + kPvAhead], hi[pi + kPvAhead]);
         constexpr int w = sfa_pv_outstanding(kPvAhead, j);
-        asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo[pi]), "+v"(hi[pi]), "+v"(pv[kk][hb]) : "i"(w));
-        const bf16x8 cv = (bf16x8){lo[pi][0], lo[pi][1], lo[pi][2], lo[pi][3], hi[pi][0], hi[pi][1], hi[pi][2], hi[pi][3]};
+        // The pair is awaited (and joined into one operand) by the first of
+        // its four MFMAs only: a wait naming it again would make the compiler
+        // assume the halves changed and copy them together before every MFMA.
+        if constexpr (hb == 0) {
+          asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo[pi]), "+v"(hi[pi]), "+v"(pv[kk][hb]) : "i"(w));
+          cv = (bf16x8){lo[pi][0], lo[pi][1], lo[pi][2], lo[pi][3], hi[pi][0], hi[pi][1], hi[pi][2], hi[pi][3]};
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(pv[kk][hb]) : "i"(w));
+        }
         o[4 * mm + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv, pv[kk][hb], o[4 * mm + hb], 0, 0, 0);
         SLI_PIN_A(o[4 * mm + hb]);
         if constexpr (kk == 0 && mm == 3) pp_issue(1, hb, pv[1][hb]);
