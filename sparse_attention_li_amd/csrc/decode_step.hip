@@ -119,11 +119,15 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
   uint32_t* const bc = reinterpret_cast<uint32_t*>(X);  // used between the phases only
 
   // 1. the indexer's chunk work; the rows of what this workgroup wrote
+  // The attention's q^T operands are loaded during the indexer's exact
+  // selection (LDS work only), so they are in registers when it ends.
   int b = 0, n_own = 0, n_chunks_b = 1;
+  bf16x8 qpre[36];
+  auto preload = [&](int bq) { sfa_load_q(s.att, bq, qpre); };
   const int st = li_decode_body<1, kStepWaves, kStepChunk, false, kStepRing, true>(
       a, IdxLds<1, kStepWaves, kStepChunk, false, kStepRing>{Z.idx.sm, X, reinterpret_cast<uint32_t*>(X + StepIdxSmem::kArena),
                                                            Z.idx.pages},
-      tag, b, Z.att.rows, &n_own, &n_chunks_b);
+      tag, b, Z.att.rows, &n_own, &n_chunks_b, preload);
   __syncthreads();  // the indexer's LDS state is dead from here on; the rows are in place
 
   if (st == kBodyShare || st == kBodyAll) {
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void li_step_kernel(const StepArgs
     const SfaBf16Lds lds{reinterpret_cast<char*>(X), reinterpret_cast<char*>(X + kTileBytes),
                          reinterpret_cast<char*>(X + 2 * kTileBytes), reinterpret_cast<char*>(X + 3 * kTileBytes),
                          Z.att.pbuf, Z.att.rows};
-    sfa_bf16_body<kStepWaves, kStepRows, true>(s.att, lds, b, c, n_own, direct);
+    sfa_bf16_body<kStepWaves, kStepRows, true>(s.att, lds, b, c, n_own, direct, qpre);
     // 3. merge, once every chunk's partial is out.  The workgroup of arrival
     // order o at the count merges items o, o + n_chunks, ...  One that gives
     // up waiting sets its bit: the last to arrive then merges its items too,

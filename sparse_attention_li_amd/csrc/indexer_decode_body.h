@@ -133,6 +133,12 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t* p, int n, uint32_t t
 // What a workgroup of li_decode_body wrote of its request's index rows.
 enum : int { kBodyNone = 0, kBodyShare = 1, kBodyAll = 2, kBodyQuit = 3 };
 
+// The hook li_decode_body calls, with the request, once its chunk's keys are
+// scored: callers that load nothing beside the selection pass this one.
+struct NoPreload {
+  __device__ void operator()(int) const {}
+};
+
 // FUSED (the single-launch decode step): the key array lives in the same LDS
 // object as the key ring, so its stores are written as LDS instructions of
 // their own (a compiler store there would wait for every tile in flight).
@@ -146,10 +152,14 @@ enum : int { kBodyNone = 0, kBodyShare = 1, kBodyAll = 2, kBodyQuit = 3 };
 // when it writes the whole request), in output order, and their number in
 // n_own (every thread; at most top_k), and the request's chunk count in
 // n_chunks_out (unless kBodyNone for padding past the last request).
-template <int NQ, int NW, int CHUNK, bool FP8, int RS, bool FUSED = false>
+// `preload` is called once per workgroup that goes on to write index rows,
+// where the selection has no global reads left (once the band is in LDS):
+// loads it issues complete under the exact selection.
+template <int NQ, int NW, int CHUNK, bool FP8, int RS, bool FUSED = false, typename Pre = NoPreload>
 __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ, NW, CHUNK, FP8, RS> lds,
                                               const uint32_t tag, int& b_out, int* rows_out = nullptr,
-                                              int* n_own = nullptr, int* n_chunks_out = nullptr) {
+                                              int* n_own = nullptr, int* n_chunks_out = nullptr,
+                                              const Pre& preload = Pre{}) {
   static_assert(!FUSED || NQ == 1, "the fused step takes one query token per request");
   IdxSmem<NQ, NW, CHUNK, FP8, RS>& sm = lds.sm;
   uint32_t* s_keys = lds.keys;  // [NQ][CHUNK]
@@ -592,7 +602,10 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       for (int i = vis[j] + tid; i < K; i += THREADS) put(&out[i], -1);
     if constexpr (FUSED) *n_own = max(0, min(CHUNK, vis[j] - s0));
   }
-  if (!any_sel) return kBodyShare;  // (every workgroup of the request decides alike: no exchange)
+  if (!any_sel) {
+    preload(b);
+    return kBodyShare;  // (every workgroup of the request decides alike: no exchange)
+  }
 
   // 1. the interval [lo_c, hi_c) holding this chunk's R-th largest key, R its quota
   uint32_t* hist = reinterpret_cast<uint32_t*>(lds.arena);  // [kHistBins] (the key ring is free now)
@@ -862,6 +875,9 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       }
       __syncthreads();
     }
+    // from here to the index stores the selection reads no global memory
+    // (with the band in LDS): the caller's loads go now
+    if (j == 0) preload(b);
     auto key_at = [&](int f) -> uint32_t {
       if (in_lds) return s_bk[f];
       const int i = chunk_of(f);

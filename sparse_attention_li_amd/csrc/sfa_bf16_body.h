@@ -96,14 +96,28 @@ struct SfaBf16Lds {
   int* rows;   // ROWS entries
 };
 
+// This lane's q^T operands of the logits (all 36 k-steps): wave w holds heads
+// 32w .. 32w+31, lane (n, half) head 32w + n, k-step k its 8 elements
+// 16k + 8 half .. +7.  Padded heads (head >= H) run on head 0's query;
+// nothing of theirs is stored.
+__device__ __forceinline__ void sfa_load_q(const SfaArgs& a, const int t, bf16x8 (&qb)[36]) {
+  const int lane = threadIdx.x & 63, head = 32 * (threadIdx.x >> 6) + (lane & 31), half = lane >> 5;
+  const bf16x8* qp =
+      reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + ((size_t)t * a.H + (head < a.H ? head : 0)) * 576);
+#pragma unroll
+  for (int k = 0; k < 36; ++k) qb[k] = qp[2 * k + half];
+}
+
 // Token t, index-row slice `split` (ROWS >= the slice's rows rounded up to
 // whole tiles).  FUSED (the single-launch step): the caller has written the
-// pool rows to attend, own_cnt of them (all valid), into lds.rows; with
-// `direct` the result is the token's output, else the partial of slot
-// `split`, written through to memory for the workgroup that merges it.
+// pool rows to attend, own_cnt of them (all valid), into lds.rows, and has
+// loaded this lane's q^T operands (sfa_load_q) into qpre; with `direct` the
+// result is the token's output, else the partial of slot `split`, written
+// through to memory for the workgroup that merges it.
 template <int NW, int ROWS, bool FUSED>
 __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds& lds, const int t, const int split,
-                                              const int own_cnt = 0, const bool direct = false) {
+                                              const int own_cnt = 0, const bool direct = false,
+                                              const bf16x8* qpre = nullptr) {
   constexpr int NT = NW * 64;
   constexpr int KS = 36;        // 16-wide k-steps of the 576-wide logits
   constexpr int MI = 16;        // 32-column output tiles
@@ -171,12 +185,11 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   const int head = 32 * wid + n;
   const bool head_ok = head < a.H;
   bf16x8 qb[KS];
-  {
-    // padded heads (head >= H) run on head 0's query; nothing of theirs is stored
-    const bf16x8* qp =
-        reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + ((size_t)t * a.H + (head_ok ? head : 0)) * 576);
+  if constexpr (FUSED) {
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qb[k] = qp[2 * k + half];
+    for (int k = 0; k < KS; ++k) qb[k] = qpre[k];
+  } else {
+    sfa_load_q(a, t, qb);
   }
   // the page ids are first used here, after the q loads have been issued
   if (!FUSED) {
@@ -309,19 +322,23 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   bf16x8 pb[2];  // P^T of the previous tile (k-blocks 0 and 1)
   pb[0] = pb[1] = (bf16x8){};
 
-  // Online softmax of one tile's S^T, in stages that the output product of
-  // the previous tile interleaves with its MFMAs.  This lane owns head n and
-  // positions 8(v/4) + 4 half + v%4.  Entries past the slice or invalid were
-  // gathered from a valid row of the slice, so their (finite) logits may
-  // enter the maximum, which is only the reference of the exponentials; their
-  // weights are zeroed.  The running reference is raised (and the
-  // accumulators rescaled) only when some head's tile maximum exceeds it by
-  // more than 2^8, so weights stay below 256 (harmless in fp32 sums and bf16
-  // operands) and most tiles skip the rescale.
+  // Online softmax of one tile's S^T, in steps that the output product of
+  // the previous tile interleaves with its MFMAs, one step per MFMA.  This
+  // lane owns head n and positions 8(v/4) + 4 half + v%4.  Entries past the
+  // slice or invalid were gathered from a valid row of the slice, so their
+  // (finite) logits may enter the maximum, which is only the reference of the
+  // exponentials; their weights are zeroed.  The running reference is raised
+  // (and the accumulators rescaled) only when some head's tile maximum exceeds
+  // it by more than 2^8, so weights stay below 256 (harmless in fp32 sums and
+  // bf16 operands) and most tiles skip the rescale.
   struct Sm {
+    float mt0, mt1;  // partial maxima of the tile (unscaled)
     float mt;        // tile maximum, scaled (both lane halves)
     float m_new, alpha, rs;
     bool need;       // the reference moves (wave-uniform)
+    float x[16];     // exponent arguments
+    float e[16];     // weights in fp32
+    float s2[8];     // pair sums
     bf16x8 p[2];     // weights, the next output product's B operands
   } sm;
   // the two lane halves hold the same head: combine across them
@@ -330,32 +347,74 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     return is_max ? fmaxf(a, b) : a + b;
   };
-  // The logits stay unscaled in sv: the scale (> 0) is applied to the
-  // maximum and folded into the exponentials' argument.
-  auto sm_stage = [&](int st, const f32x16& sv) {
-    if (st == 0) {
-      sm.mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    } else if (st == 1) {
-      const float m = fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15])));
-      sm.mt = fmaxf(sm.mt, m);
-    } else if (st == 2) {
-      sm.mt *= sl2;
-    } else if (st == 3) {
+  // Step j of the softmax.  The logits stay unscaled in sv: the scale (> 0)
+  // is applied to the maximum and folded into the exponentials' argument.
+  // A step takes at most one exponential and three other vector operations,
+  // none of which uses a result of the same step: the in-order issue then
+  // never holds the next MFMA behind a dependent chain, and the work fits in
+  // the shadow of the MFMA before it.  Value v's argument is formed at step
+  // 8 + v, its exponential at 9 + v; the weights of pair q are summed at
+  // 11 + 2q, and the sum is added and the pair converted to bf16 at 12 + 2q.
+  auto sm_step = [&](int j, const f32x16& sv) {
+    // (each result is pinned where it is made: the compiler would otherwise
+    // gather the arithmetic next to its first use, many steps later)
+    if (j == 0) {
+      sm.mt0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+      sm.mt1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+      SLI_PIN_V(sm.mt0);
+      SLI_PIN_V(sm.mt1);
+    } else if (j == 1) {
+      sm.mt0 = fmaxf(fmaxf(sm.mt0, sv[6]), sv[7]);
+      sm.mt1 = fmaxf(fmaxf(sm.mt1, sv[8]), sv[9]);
+      SLI_PIN_V(sm.mt0);
+      SLI_PIN_V(sm.mt1);
+    } else if (j == 2) {
+      sm.mt0 = fmaxf(fmaxf(sm.mt0, sv[10]), sv[11]);
+      sm.mt1 = fmaxf(fmaxf(sm.mt1, sv[12]), sv[13]);
+      SLI_PIN_V(sm.mt0);
+      SLI_PIN_V(sm.mt1);
+    } else if (j == 3) {
+      sm.mt0 = fmaxf(fmaxf(sm.mt0, sv[14]), sv[15]);
+      SLI_PIN_V(sm.mt0);
+    } else if (j == 4) {
+      sm.mt = fmaxf(sm.mt0, sm.mt1) * sl2;
+      SLI_PIN_V(sm.mt);
+    } else if (j == 5) {
       sm.mt = halves(sm.mt, true);
+      SLI_PIN_V(sm.mt);
+    } else if (j == 6) {
       sm.need = __ballot(sm.mt > m_run + 8.f) != 0;
       sm.m_new = sm.need ? fmaxf(m_run, sm.mt) : m_run;
+      SLI_PIN_V(sm.m_new);
+    } else if (j == 7) {
       sm.alpha = __builtin_amdgcn_exp2f(m_run - sm.m_new);
       sm.rs = 0.f;
-    } else if (st >= 4 && st < 12) {
-      const int v = 2 * (st - 4);
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], sl2, -sm.m_new));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v + 1], sl2, -sm.m_new));
-      sm.rs += p0 + p1;
-      sm.p[v >> 3][v & 7] = (__bf16)p0;
-      sm.p[v >> 3][(v & 7) + 1] = (__bf16)p1;
+      SLI_PIN_V(sm.alpha);
+    }
+    if (j >= 8 && j < 24) {
+      sm.x[j - 8] = __builtin_fmaf(sv[j - 8], sl2, -sm.m_new);
+      SLI_PIN_V(sm.x[j - 8]);
+    }
+    if (j >= 9 && j < 25) {
+      sm.e[j - 9] = __builtin_amdgcn_exp2f(sm.x[j - 9]);
+      SLI_PIN_V(sm.e[j - 9]);
+    }
+    if (j >= 11 && j < 26 && (j - 11) % 2 == 0) {
+      const int q = (j - 11) / 2;
+      sm.s2[q] = sm.e[2 * q] + sm.e[2 * q + 1];
+      SLI_PIN_V(sm.s2[q]);
+    }
+    if (j >= 12 && j < 27 && (j - 12) % 2 == 0) {
+      const int q = (j - 12) / 2, v = 2 * q;
+      sm.rs += sm.s2[q];
+      sm.p[v >> 3][v & 7] = (__bf16)sm.e[v];
+      sm.p[v >> 3][(v & 7) + 1] = (__bf16)sm.e[v + 1];
+      SLI_PIN_V(sm.rs);
+      SLI_PIN_V(sm.p[v >> 3]);
     }
   };
-  constexpr int SM_STAGES = 12;
+  constexpr int SM_STEPS = 27;
+  static_assert(SM_STEPS <= PVS, "the softmax steps fit between the output MFMAs");
   // finishes the tile's softmax once the previous output product is done:
   // zero the weights of invalid entries (rare), rescale, fold the sum
   auto sm_finish = [&](uint32_t vmask) {
@@ -496,8 +555,8 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
         SLI_PIN_A(o[4 * mm + hb]);
         if constexpr (kk == 0 && mm == 3) pp_issue(1, hb, pv[1][hb]);
       }
-      if constexpr (j % 2 == 1 && j / 2 < SM_STAGES) {
-        if (do_sm) sm_stage(j / 2, sv);
+      if constexpr (j < SM_STEPS) {
+        if (do_sm) sm_step(j, sv);
       }
       // The next tile's loads go between these independent MFMAs, one every
       // third step (four waves then issue one about every 25 cycles, within
