@@ -399,6 +399,10 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     if (steady || t + 3 < n_tiles) issue(t + 3, pg_next);
+    // the next page id (a scalar load) is requested now, so its latency
+    // passes under this step's matrix work rather than at the next step's
+    // wait, which also covers scalar loads
+    pg_next = page(t + 4);
     const bool cur = steady || t < n_tiles;
     const bool prev = steady || (t >= 1 && t - 1 < n_tiles);
     const bool next = steady || t + 1 < n_tiles;
@@ -428,7 +432,6 @@ __global__ __launch_bounds__(kPfThreads) void li_prefill_kernel(const IdxPrefill
     // the query's first wave filters tile t-2 (both partials visible since
     // this step's barrier) after its own matrix work is issued
     if (fin && (steady || (t >= 2 && t - 2 < n_tiles))) finish(t - 2);
-    pg_next = page(t + 4);  // scalar load, used one step later
     if (fin && cnt > kPfCap - kPfTile) {
       __builtin_amdgcn_s_waitcnt(0xC07F);
       compact();
