@@ -899,7 +899,11 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       tau = sm.sel[2];
       ngt = (int)sm.sel[3];
     } else {
-      tau = in_lds ? block_radix_select<kBandCap / THREADS>(key_at, (int)NB, need, sm.hist, sm.sel, ngt)
+      // (the band in LDS is read through an accessor with no global path: a
+      // read that might also be a global load makes the compiler wait for
+      // every memory operation in flight before each LDS read)
+      tau = in_lds ? block_radix_select<kBandCap / THREADS>([&](int f) { return s_bk[f]; }, (int)NB, need, sm.hist,
+                                                            sm.sel, ngt)
                    : block_radix_select_big(key_at, (int)NB, need, sm.hist, sm.sel, ngt);
     }
     const uint32_t ties = (uint32_t)(need - ngt);  // keys equal to tau that are taken, lowest positions first
@@ -907,22 +911,27 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
 
     if (mode == kModeNormal) {
       // band entries before this chunk: how many are > tau, how many tie
-      // (from global memory: eight reads per thread in flight)
+      // (eight reads per thread in flight; the LDS and global forms are
+      // separate loops, so the LDS reads wait for nothing but themselves)
       uint32_t gt = 0, eq = 0;
       const int cb = (int)cbase[c];
       constexpr int LPT = 8;
+      auto count = [&](auto get) {
 #pragma unroll 1
-      for (int f0 = tid; f0 < cb; f0 += LPT * THREADS) {
-        uint32_t kv[LPT];
+        for (int f0 = tid; f0 < cb; f0 += LPT * THREADS) {
+          uint32_t kv[LPT];
 #pragma unroll
-        for (int r = 0; r < LPT; ++r) kv[r] = f0 + r * THREADS < cb ? key_at(f0 + r * THREADS) : 0u;
+          for (int r = 0; r < LPT; ++r) kv[r] = f0 + r * THREADS < cb ? get(f0 + r * THREADS) : 0u;
 #pragma unroll
-        for (int r = 0; r < LPT; ++r) {
-          const bool in = f0 + r * THREADS < cb;
-          gt += (in && kv[r] > tau) ? 1u : 0u;
-          eq += (in && kv[r] == tau) ? 1u : 0u;
+          for (int r = 0; r < LPT; ++r) {
+            const bool in = f0 + r * THREADS < cb;
+            gt += (in && kv[r] > tau) ? 1u : 0u;
+            eq += (in && kv[r] == tau) ? 1u : 0u;
+          }
         }
-      }
+      };
+      if (in_lds) count([&](int f) { return s_bk[f]; });
+      else count(key_at);
       // own keys in position order: selected for certain (>= hi, or in the
       // band and > tau) or tied at tau
       uint32_t kk[PER], nd = 0, nt = 0;
