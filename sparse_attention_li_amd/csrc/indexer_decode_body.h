@@ -37,6 +37,10 @@
 //      the positions), selects kappa among them exactly (radix select,
 //      need = K - #keys >= hi), counts what the chunks before it select, and
 //      writes its own selected positions at that offset, in position order.
+//      In one-token grids of several rounds only the last chunk to publish
+//      does this, for the whole request (merging the two sorted position
+//      lists: keys >= hi and the selected band); the others leave after
+//      publishing, and their CUs take the next round's chunks.
 // The exchanges are arrival counters with bounded waits.  A workgroup whose
 // first wait times out (its request's chunks were not all resident) publishes
 // every key as band, which keeps the result exact; one whose second wait
@@ -760,9 +764,35 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
       if (vis[j] > K) xstore64(&a.cnts[(size_t)(t0 + j) * ncm + c], tagged(sm.flag[2 + (j & 1)], tag));
     old2 = __hip_atomic_fetch_add(&ctr[kArrive2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // exchange 2: every chunk's counts
+  // One-token grids of several rounds (the XCD-local layout) hand the whole
+  // request to the last chunk to publish: the others leave at once, so their
+  // CU takes the next round's chunks instead of idling through the
+  // exchange-2 wait and a selection every chunk of the request would repeat
+  // (mixed-length FP8 workload 201.8 -> 195.1 us).  Two-token calls keep the
+  // shared selection: there the last chunk's longer stay (two selections)
+  // delays the dispatch of the next request's chunks, which then wait for it
+  // at exchange 1 (128 x 128K two-token: 749 -> 823 us).  Grids of one round
+  // keep every chunk busy to the end.  (Needs the keys' LDS for the two
+  // position lists of the write-out.)
+  const bool lastw = !FUSED && NQ == 1 && a.xcd_local && NQ * CHUNK >= 2 * K;
   uint32_t cnt_v[NQ];
-  {
+  if (lastw) {
+    if (tid == 0) {
+      const bool last = old2 == (uint32_t)n_chunks - 1;
+      if (last) __hip_atomic_store(&ctr[kArrive2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.flag[1] = last ? kModeFull : kModeQuit;
+    }
+    __syncthreads();
+    if (sm.flag[1] == kModeQuit) return kBodyQuit;
+    // every chunk has published (its count is issued before its arrival)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      cnt_v[j] = 0u;
+      if (vis[j] > K && tid < n_chunks)
+        poll_tagged(&a.cnts[(size_t)(t0 + j) * ncm + tid], 1, tag, 1 << 30, &cnt_v[j]);
+    }
+    __syncthreads();
+  } else {
     bool ok = true;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
@@ -795,7 +825,7 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
   }
   const uint32_t mode = sm.flag[1];
   if (mode == kModeQuit) return kBodyQuit;
-  if (sm.flag[0] == 0u) {
+  if (!lastw && sm.flag[0] == 0u) {
     // the last one has arrived, so every count is in memory: read them again
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
@@ -909,7 +939,97 @@ __device__ __forceinline__ int li_decode_body(const IdxDecodeArgs& a, IdxLds<NQ,
     const uint32_t ties = (uint32_t)(need - ngt);  // keys equal to tau that are taken, lowest positions first
     int32_t* out = a.idx_out + tok * K;
 
-    if (mode == kModeNormal) {
+    if (lastw) {
+      // The whole request from the published lists: every chunk's keys >= hi
+      // (all selected; in chunk order they are in position order) and the
+      // selected band entries (> tau, or tied at tau up to `ties` of them,
+      // lowest positions first; the flat band is in position order too).
+      // Both lists are sorted, so a position's output slot is its rank in its
+      // own list plus the number of the other list's positions below it.  The
+      // keys' LDS is free (every chunk's keys are in the lists).
+      int32_t* const above_pos = reinterpret_cast<int32_t*>(s_keys);  // [A]
+      int32_t* const band_pos = above_pos + K;                        // [need]
+      auto seg_of = [&](const uint32_t* base, int f) {  // largest i < n_chunks with base[i] <= f
+        int lo = 0, hi = n_chunks;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)base[mid] <= f) lo = mid; else hi = mid;
+        }
+        return lo;
+      };
+      {
+        // chunk i's keys >= hi sit at the back of its list, in position order
+        // from the last slot down; eight loads per thread in flight
+        constexpr int LPT = 8;
+#pragma unroll 1
+        for (int f0 = 0; f0 < (int)A; f0 += LPT * THREADS) {
+          uint64_t ev[LPT];
+#pragma unroll
+          for (int r = 0; r < LPT; ++r) {
+            const int f = f0 + tid + r * THREADS;
+            ev[r] = 0ull;
+            if (f < (int)A) {
+              const int i = seg_of(abase, f);
+              ev[r] = xload64(&a.cand[gaddr(i, CHUNK - 1 - (f - (int)abase[i]))]);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < LPT; ++r) {
+            const int f = f0 + tid + r * THREADS;
+            if (f < (int)A) above_pos[f] = (int32_t)(ev[r] >> 32);
+          }
+        }
+      }
+      // the selected band entries, compacted in order: an entry > tau, or the
+      // tie of rank < ties; its slot = selected entries before it
+      uint32_t n_sel = 0, eq_seen = 0;
+      auto compact = [&](auto get) {
+#pragma unroll 1
+        for (int fb = 0; fb < (int)NB; fb += THREADS) {
+          const int f = fb + tid;
+          const uint64_t ev = f < (int)NB ? get(f) : 0ull;
+          const uint32_t key = (uint32_t)ev;
+          const bool in = f < (int)NB;
+          const bool gt = in && key > tau, tie = in && key == tau;
+          uint32_t gt_tot, tie_pre, tie_tot;
+          const uint32_t gt_pre = block_excl_scan2(gt ? 1u : 0u, tie ? 1u : 0u, sm.scan, gt_tot, tie_pre, tie_tot);
+          const uint32_t avail = ties > eq_seen ? ties - eq_seen : 0u;  // ties still to take
+          if (gt || (tie && tie_pre < avail)) {
+            const uint32_t slot = n_sel + gt_pre + min(tie_pre, avail);
+            if (slot < (uint32_t)K) band_pos[slot] = (int32_t)(ev >> 32);
+          }
+          n_sel += gt_tot + min(tie_tot, avail);
+          eq_seen += tie_tot;
+        }
+      };
+      if (in_lds)
+        compact([&](int f) { return (uint64_t)s_bk[f] | ((uint64_t)(uint32_t)s_bp[f] << 32); });
+      else
+        compact([&](int f) {
+          const int i = chunk_of(f);
+          return xload64(&a.cand[gaddr(i, f - cbase[i])]);
+        });
+      __syncthreads();
+      const int n_band = min((int)n_sel, K - (int)A);  // = need
+      auto below = [](const int32_t* list, int n, int p) {  // entries of a sorted list below p
+        int lo = 0, hi = n;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (list[mid] < p) lo = mid + 1; else hi = mid;
+        }
+        return lo;
+      };
+      for (int f = tid; f < (int)A; f += THREADS) {
+        const int p = above_pos[f];
+        const int o = f + below(band_pos, n_band, p);
+        if (o < K) put(&out[o], p);
+      }
+      for (int g = tid; g < n_band; g += THREADS) {
+        const int p = band_pos[g];
+        const int o = g + below(above_pos, (int)A, p);
+        if (o < K) put(&out[o], p);
+      }
+    } else if (mode == kModeNormal) {
       // band entries before this chunk: how many are > tau, how many tie
       // (eight reads per thread in flight; the LDS and global forms are
       // separate loops, so the LDS reads wait for nothing but themselves)

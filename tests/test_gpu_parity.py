@@ -354,6 +354,42 @@ def test_band_beyond_16_bits_with_fallbacks(li, spin):
         li.li_set_exchange_patience(-1)
 
 
+@pytest.mark.parametrize("kind", ["trend", "zero_query"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_whole_request_writer_xcd_local(li, fmt, kind):
+    """One-token grids of several rounds (24 requests x 12 chunks of 4096
+    positions, the XCD-local layout) leave each request to the last chunk to
+    publish, which writes the whole index row by merging the keys above the
+    band with the band entries it selects.  Scores that rise (even requests)
+    or fall (odd ones) with position make the band wider than its LDS copy
+    (the selection reads the lists in memory); a zero query makes every score
+    equal, so the K lowest positions must be written (ties in position order
+    across chunks).  Indices must equal the oracle's."""
+    B, L, K = 24, 49152, 1500
+    case = synth.Case(seed=43, B=B, n_q=1, seq_lens=[L] * B, top_k=K, H=16, idx_fmt=fmt,
+                      kv_fmt="fp8" if fmt != "bf16" else "bf16")
+    g = GpuCase(case, attention=False)
+    q_int = np.zeros((B, 64, 128), np.int8) if kind == "zero_query" else np.ones((B, 64, 128), np.int8)
+    w = np.full((B, 64), 0.5, np.float32)
+    k_int = [_trend_keys(L, b % 2 == 0, 100 + b) for b in range(B)]
+    q, qs, ks = encode_indexer_int(case, q_int, k_int)
+    load_indexer(g, q, qs, w, ks)
+    q_fmt = "bf16" if fmt == "bf16" else "fp8"
+    refs = []
+    for b in range(B):
+        if kind == "zero_query":
+            refs.append(np.arange(K))
+            continue
+        sc = oracle.index_scores(q[b], w[b], ks[b][0], L, q_fmt=q_fmt, q_scales=None if qs is None else qs[b],
+                                 k_fmt=fmt, k_scales=ks[b][1])
+        ridx, n = oracle.topk(sc, K)
+        refs.append(np.sort(ridx[:n]))
+    for _ in range(2):  # the second call runs on the state the first left
+        idx = g.score_topk(li).cpu().numpy()
+        for b in range(B):
+            assert (idx[b] == refs[b]).all(), f"request {b}"
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_two_token_call_equals_one_token_calls(li, fmt):
     """Token j of a two-token (draft-and-verify) call sees L - 1 + j positions:
