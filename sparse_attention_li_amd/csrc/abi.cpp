@@ -82,14 +82,16 @@ int spin_max() { return g_patience.load(std::memory_order_relaxed); }
 
 // Splits of the index row so that about one workgroup per CU is busy (an
 // attention workgroup fills a CU: one wave per SIMD).  bf16 workgroups hold
-// every head of a token; FP8 ones a block of up to 64 heads.
+// every head of a token; FP8 ones a block of up to 64 heads.  Small calls
+// split down to one 32-row tile per workgroup (batch 1 x 2048, top-K 256:
+// 8 splits, 16.8 -> 13.5 us against two-tile splits).
 void sfa_shape(int T, int H, int top_k, bool fp8, int& n_splits, int& split_len) {
   const int cus = device_cus();
   const int hpb = sli::sfa_heads_per_block(H, fp8);
   const int head_blocks = (H + hpb - 1) / hpb;
   const int per_split = T * head_blocks;
   int s = std::max(1, (cus + per_split - 1) / per_split);
-  s = std::min(s, std::max(1, top_k / 64));
+  s = std::min(s, std::max(1, top_k / 32));
   split_len = (top_k + s - 1) / s;
   split_len = (split_len + 31) / 32 * 32;
   split_len = std::min(split_len, sli::kMaxSplitRows);

@@ -36,7 +36,10 @@ static hipError_t launch_one(const IdxDecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_idx_decode(const IdxDecodeArgs& a, int chunk, bool fp8, hipStream_t stream) {
-  if (chunk == 1024) {
+  if (chunk == 256) {
+    if (a.n_q == 1) return fp8 ? launch_one<1, 4, 256, true>(a, stream) : launch_one<1, 4, 256, false>(a, stream);
+    if (a.n_q == 2) return fp8 ? launch_one<2, 4, 256, true>(a, stream) : launch_one<2, 4, 256, false>(a, stream);
+  } else if (chunk == 1024) {
     if (a.n_q == 1) return fp8 ? launch_one<1, 4, 1024, true>(a, stream) : launch_one<1, 4, 1024, false>(a, stream);
     if (a.n_q == 2) return fp8 ? launch_one<2, 4, 1024, true>(a, stream) : launch_one<2, 4, 1024, false>(a, stream);
   } else if (chunk == 2048) {

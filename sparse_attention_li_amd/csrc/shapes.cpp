@@ -4,7 +4,11 @@
 
 namespace sli {
 
-// Positions per workgroup.  4096 (eight waves, one workgroup per CU) when
+// Positions per workgroup.  256 for grids that would leave most of the chip
+// idle even at 1024 (a short request or two, up to 65536 positions: the
+// largest chunk count a request may have): a chunk's 64 KiB of bf16 keys are
+// then in flight at once, and the latency of a small call is one memory round
+// trip of streaming instead of four.  4096 (eight waves, one workgroup per CU) when
 // the grid still gives every CU a workgroup: each CU then streams the same
 // amount and the request's chunks finish together.  FP8 one-token grids that
 // would take more than one round of the chip at 4096 (three four-wave
@@ -17,6 +21,7 @@ int idx_decode_chunk(int B, int n_q, bool fp8, int max_pages, int cus) {
   const long long maxlen = (long long)max_pages * 64;
   auto wgs = [&](long long ch) { return (long long)B * ((maxlen + ch - 1) / ch); };
   if (fp8 && n_q == 1 && wgs(4096) > 3LL * cus) return 8192;
+  if (wgs(256) <= cus && maxlen <= 256LL * kMaxChunksPerSeq) return 256;
   if ((n_q == 1 || fp8) && wgs(4096) >= cus) return 4096;
   return wgs(1024) > 2LL * cus ? 2048 : 1024;
 }

@@ -62,7 +62,7 @@ void seqs(const int32_t* seq_lens, const int32_t* bt, int B, int max_pages) {
 }
 
 void idx_decode(const sli::IdxDecodeArgs& a, int chunk, bool fp8) {
-  if (chunk != 1024 && chunk != 2048 && chunk != 4096 && chunk != 8192) die("chunk length");
+  if (chunk != 256 && chunk != 1024 && chunk != 2048 && chunk != 4096 && chunk != 8192) die("chunk length");
   if ((long long)a.n_chunks_max * chunk < (long long)a.max_pages * 64) die("chunks do not cover max_pages");
   if (a.n_chunks_max > sli::kMaxChunksPerSeq || a.B > sli::kMaxSeqs) die("grid limits");
   const size_t T = (size_t)a.B * a.n_q, E = fp8 ? 1 : 2, ncm = (size_t)a.n_chunks_max;
