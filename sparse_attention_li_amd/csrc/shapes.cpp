@@ -4,11 +4,11 @@
 
 namespace sli {
 
-// Positions per workgroup.  256 for grids that would leave most of the chip
-// idle even at 1024 (a short request or two, up to 65536 positions: the
-// largest chunk count a request may have): a chunk's 64 KiB of bf16 keys are
-// then in flight at once, and the latency of a small call is one memory round
-// trip of streaming instead of four.  4096 (eight waves, one workgroup per CU) when
+// Positions per workgroup.  256 when even at that length the grid fits one
+// round of the chip (small calls: a few requests of up to 65536 positions,
+// the most chunks a request may have): a chunk's 64 KiB of bf16 keys are then
+// in flight at once, and a small call streams in one memory round trip
+// instead of four.  4096 (eight waves, one workgroup per CU) when
 // the grid still gives every CU a workgroup: each CU then streams the same
 // amount and the request's chunks finish together.  FP8 one-token grids that
 // would take more than one round of the chip at 4096 (three four-wave
