@@ -26,7 +26,7 @@ HIP_FLAGS = [
 # awaited by explicit lgkmcnt waits: the compiler does not know such a
 # register is still being written until the wait, so the build scans their
 # assembly for any use of it in between (lds_hazards.py).
-LDS_CHECKED = {"sfa.hip": ("sfa_bf16_kernel",), "indexer_decode.hip": ("li_decode_kernel",),
+LDS_CHECKED = {"sfa.hip": ("sfa_bf16_kernel", "sfa_f8_kernel"), "indexer_decode.hip": ("li_decode_kernel",),
                "decode_step.hip": ("li_step_kernel",)}
 
 

@@ -412,7 +412,36 @@ static hipError_t launch_sfa_bf16(const SfaArgs& a, hipStream_t stream) {
   return e != hipSuccess ? e : launch_combine(a, stream);
 }
 
+// FP8 latent rows of 576 bytes (E4M3 codes, block scales apart), every head
+// of the token in one workgroup: the same body and block layout, with three
+// bf16 slots that the waves fill by converting their own gathered rows.
+__global__ __launch_bounds__(256) void sfa_f8_kernel(const SfaArgs a) {
+  __shared__ __attribute__((aligned(128))) char slot0[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char slot1[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char slot2[kTileBytes];
+  __shared__ __attribute__((aligned(128))) char raw[4 * kF8Wave];
+  __shared__ __attribute__((aligned(128))) char raw_sc[4 * 256];
+  __shared__ __attribute__((aligned(128))) char pbuf[4 * 2 * 64 * 16];
+  __shared__ int rows[kMaxSplitRows];
+  const int x = blockIdx.x & 7, g = blockIdx.x >> 3;
+  const int tpx = (a.T + 7) / 8;
+  const int t = x * tpx + g / a.n_splits;
+  const int split = g % a.n_splits;
+  if (t >= a.T) return;
+  sfa_bf16_body<4, kMaxSplitRows, false, true>(
+      a, SfaBf16Lds{slot0, slot1, slot2, nullptr, pbuf, rows, raw, raw_sc}, t, split);
+}
+
+// FP8 rows of 576 bytes, every head of the token (65 to 128) in one workgroup.
+static hipError_t launch_sfa_f8(const SfaArgs& a, hipStream_t stream) {
+  dim3 grid(8 * ((a.T + 7) / 8) * a.n_splits);
+  hipLaunchKernelGGL(sfa_f8_kernel, grid, dim3(4 * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_combine(a, stream);
+}
+
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream) {
+  if (fp8 && !a.rope_bf16 && a.H > 64) return launch_sfa_f8(a, stream);
   if (fp8 && a.rope_bf16)
     return a.H <= 32 ? launch_sfa_blocks<1, true, true>(a, stream) : launch_sfa_blocks<2, true, true>(a, stream);
   if (fp8) return a.H <= 32 ? launch_sfa_blocks<1, true>(a, stream) : launch_sfa_blocks<2, true>(a, stream);

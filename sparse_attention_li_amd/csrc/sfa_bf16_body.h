@@ -87,6 +87,8 @@ static_assert(sfa_pv_schedule_ok(1) && sfa_pv_schedule_ok(2), "output-product re
 // LDS of the all-heads body: four ring slots of one tile each (the targets
 // of the direct-to-LDS gathers; no C++ access may touch a slot while loads
 // into any slot are in flight), the weights buffer and the slice's row ids.
+// FP8 rows use three bf16 slots (slot3 unused) and a raw slot: the codes of
+// the next tile (4 x kF8Wave bytes) and their block scales (4 x 256 bytes).
 struct SfaBf16Lds {
   char* slot0;
   char* slot1;
@@ -94,7 +96,54 @@ struct SfaBf16Lds {
   char* slot3;
   char* pbuf;  // 4 * 2 * 64 * 16 bytes
   int* rows;   // ROWS entries
+  char* raw = nullptr;
+  char* raw_sc = nullptr;
 };
+constexpr int kF8Wave = 5 * 1024;  // raw bytes per wave: its 8 rows x 576 (4.5 KiB) + padding
+
+// Schedule of the dequantisation that the FP8 variant interleaves with the
+// 36 logit MFMAs (steps 0..35) of the current tile.  Unit j (of five per
+// lane) is converted and stored a quarter (8 bytes of bf16) per step at
+// steps 1 + 7j .. 4 + 7j.  Its codes, block
+// scale and the pool row of the same unit of the tile after next are read
+// at step 7j - 3 (before step 0 for unit 0; the row of the scale gather with
+// unit 4) and awaited at step 7j; its gather of the tile after next goes out
+// at step 7j + 1, into the bytes just read, and the scale gather at step 29,
+// after the last scale read.  DS operations in issue order: before step 0
+// unit 0's three reads and the first PDL logit operand reads; at step s the
+// operand read of k-step s + PDL, then a unit's reads, then the step's store.
+// Each step's wait leaves in flight only operations issued after everything
+// that step and the next one use.
+__host__ __device__ constexpr bool sfa_f8_store_at(int s) { return s >= 1 && (s - 1) % 7 < 4 && (s - 1) / 7 < 5; }
+__host__ __device__ constexpr bool sfa_f8_read_at(int s) { return s >= 4 && (s + 3) % 7 == 0 && (s + 3) / 7 <= 4; }
+__host__ __device__ constexpr int sfa_f8_reads_at(int s) { return sfa_f8_read_at(s) ? ((s + 3) / 7 == 4 ? 4 : 3) : 0; }
+__host__ __device__ constexpr int sfa_f8_ops_at(int pdl, int s) {
+  return (s + pdl < 36 ? 1 : 0) + sfa_f8_reads_at(s) + (sfa_f8_store_at(s) ? 1 : 0);
+}
+__host__ __device__ constexpr int sfa_f8_ops_before(int pdl, int s) {
+  int n = 3 + pdl;
+  for (int i = 0; i < s; ++i) n += sfa_f8_ops_at(pdl, i);
+  return n;
+}
+// position of the last operation the wait at step k must see completed
+__host__ __device__ constexpr int sfa_f8_need(int pdl, int k) {
+  int need = k < pdl ? 3 + k : sfa_f8_ops_before(pdl, k - pdl);  // logit operand k
+  if (k >= 7 && k <= 28 && k % 7 == 0) {  // unit k / 7: its reads at step k - 3
+    const int idx = sfa_f8_ops_before(pdl, k - 3) + (k - 3 + pdl < 36 ? 1 : 0) + sfa_f8_reads_at(k - 3) - 1;
+    need = need > idx ? need : idx;
+  }
+  return need;
+}
+__host__ __device__ constexpr int sfa_f8_outstanding(int pdl, int k) {
+  return sfa_f8_ops_before(pdl, k + 1) - sfa_f8_need(pdl, k) - 1;
+}
+__host__ __device__ constexpr bool sfa_f8_schedule_ok(int pdl) {
+  for (int k = 0; k < 36; ++k) {
+    const int w = sfa_f8_outstanding(pdl, k);
+    if (w < 0 || w > 15) return false;
+  }
+  return true;
+}
 
 // This lane's q^T operands of the logits (all 36 k-steps): wave w holds heads
 // 32w .. 32w+31, lane (n, half) head 32w + n, k-step k its 8 elements
@@ -114,7 +163,7 @@ __device__ __forceinline__ void sfa_load_q(const SfaArgs& a, const int t, bf16x8
 // loaded this lane's q^T operands (sfa_load_q) into qpre; with `direct` the
 // result is the token's output, else the partial of slot `split`, written
 // through to memory for the workgroup that merges it.
-template <int NW, int ROWS, bool FUSED>
+template <int NW, int ROWS, bool FUSED, bool F8 = false>
 __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds& lds, const int t, const int split,
                                               const int own_cnt = 0, const bool direct = false,
                                               const bf16x8* qpre = nullptr) {
@@ -130,6 +179,8 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   static_assert(PDL <= 4, "explicit LDS-read waits cover at most 4 steps in flight");
   static_assert(NW == 4, "four head blocks and four column quarters");
   static_assert(ROWS % NT == 0, "row ids resolved in whole passes");
+  static_assert(!(F8 && FUSED), "FP8 rows only in the attention launch");
+  static_assert(!F8 || sfa_f8_schedule_ok(PDL), "dequantisation schedule");
   char* const slot0 = lds.slot0;
   char* const slot1 = lds.slot1;
   char* const slot2 = lds.slot2;
@@ -139,9 +190,10 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // The last 4 KiB of a slot hold the tile's rope columns, read only by the
   // logits; once every wave is past them they carry the tile's softmax
   // rescale factors (128 floats at +0, one flag per head block at +512).  The
-  // prologue's minimum row sits there in slot 3 (no tile has been loaded yet).
+  // prologue's minimum row sits there in the last slot (no tile has been
+  // loaded yet).
   constexpr int kRope = 32768;
-  int* const s_fallback = reinterpret_cast<int*>(slot3 + kRope);
+  int* const s_fallback = reinterpret_cast<int*>((F8 ? slot2 : slot3) + kRope);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 31, half = lane >> 5, gi = lane & 15;
   const int b = t / a.n_q;
@@ -226,6 +278,10 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // each load is one per-row base address plus an immediate offset.
   const int c_lane = (lane & 7) ^ swz(lane >> 3);
   auto ring = [&](int tile) -> char* {
+    if constexpr (F8) {
+      const int i = tile % 3;
+      return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+    }
     const int i = tile & 3;
     return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3;
   };
@@ -236,28 +292,91 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     for (int r = 0; r < RPW; ++r) pr[r] = rows[tile * kTileRows + 8 * (wid + NW * r) + (lane >> 3)];
   };
   // With four waves a lane copies one row per tile (tile < tiles unless it
-  // is a prologue load).  The loads go through a buffer resource over the
-  // pool with one 1152-byte record per latent row: the row is the index, the
-  // lane's chunk the per-lane offset and load k's 128-byte step the
-  // wave-uniform offset, so a load costs no per-lane address arithmetic.
+  // is a prologue load): the lane's address is its row's start plus its
+  // chunk plus load k's 128-byte step.  (64-bit addresses: a pool may exceed
+  // the 4 GiB a buffer resource spans.  The step is added to the address, not
+  // given as the instruction's offset, which would move the LDS destination
+  // too.)
   static_assert(RPW == 1, "one row per lane and tile");
-  const uint32_t pool_rows = (uint32_t)min((long long)a.num_pages * 64, 0xffffffffll);
-  const auto kv_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kv), (short)1152, (int)pool_rows, 0x00020000);
   const uint32_t c16 = 16 * c_lane;
   const int wid_s = __builtin_amdgcn_readfirstlane(wid);
   auto tile_row = [&](int tile, const int (&pr)[4]) -> int { return (pr[0] >= 0 && tile < tiles) ? pr[0] : fb_row; };
+  auto row_src = [&](int row) -> const char* { return static_cast<const char*>(a.kv) + (size_t)row * 1152 + c16; };
   // load k of this wave into the tile at dst (= its slot + 1 KiB x wave)
-  auto load_one = [&](char* dst, int row, int k) {
-    __builtin_amdgcn_struct_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + 1024 * NW * k), 16, row, c16, 128 * k, 0, 0);
+  auto load_one = [&](char* dst, const char* src, int k) {
+    __builtin_amdgcn_global_load_lds(src + 128 * k, (lds_void*)(dst + 1024 * NW * k), 16, 0, 0);
   };
   auto issue = [&](int tile) {
     int pr[4];
     tile_rows(tile, pr);
-    const int row = tile_row(tile, pr);
+    const char* src = row_src(tile_row(tile, pr));
     char* dst = ring(tile) + 1024 * wid_s;
 #pragma unroll
-    for (int k = 0; k < DPW; ++k) load_one(dst, row, k);
+    for (int k = 0; k < DPW; ++k) load_one(dst, src, k);
+  };
+
+  // FP8 rows: 576 bytes = 36 16-byte units of E4M3 codes (512 latent, 64
+  // rope), with kv_groups f32 block scales per row kept apart.  Wave w
+  // gathers its own rows 8w .. 8w+7 of a tile (units in order, lane l of load
+  // j taking unit l + 64 j; the fifth load's upper lanes fetch the last unit
+  // again into padding) and their scales into its part of the raw slot, and
+  // later converts exactly those bytes into the bf16 tile: a wave never waits
+  // for another wave's gather, and the raw slot needs no barrier.
+  // (the per-lane unit offsets are recomputed where used, from a lane index
+  // the compiler cannot hoist: kept live across the loop they would push the
+  // q operands out of registers)
+  const int G = F8 ? a.kv_groups : 1;
+  auto f8_lane = [&]() -> int {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  auto f8_unit = [](int j, int ln) -> int { return j < 4 ? ln + 64 * j : min(256 + ln, 287); };
+  // block scale of a unit (units 32..35 are the rope codes, scale group 4)
+  auto f8_group = [&](int ch) -> int { return G == 1 ? 0 : min(ch >> 3, 4); };
+  // this lane's scale entry: row 8w + sl / G, group sl % G (sl = min(lane, 8G - 1))
+  int f8_pr[6];  // pool rows of this lane's five units and of its scale entry
+  auto f8_rows = [&](int tile) {
+    const int ln = f8_lane(), sl = min(ln, 8 * G - 1);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int rw = j < 5 ? f8_unit(j, ln) / 36 : (G == 1 ? sl : sl / 5);
+      const int pr = tile < tiles ? rows[tile * kTileRows + 8 * wid + rw] : -1;
+      f8_pr[j] = pr >= 0 ? pr : fb_row;
+    }
+  };
+  // gather j (0..4: codes, 5: scales) of the tile whose rows f8_rows resolved
+  auto f8_load = [&](int j, int ln) {
+    if (j < 5) {
+      const int u = f8_unit(j, ln);
+      const char* src = static_cast<const char*>(a.kv) + (size_t)f8_pr[j] * 576 + 16 * (u % 36);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds.raw + kF8Wave * wid_s + 1024 * j), 16, 0, 0);
+    } else {
+      const int sl = min(ln, 8 * G - 1);
+      const float* src = a.kv_scales + (size_t)f8_pr[5] * G + (G == 1 ? 0 : sl % 5);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds.raw_sc + 256 * wid_s), 4, 0, 0);
+    }
+  };
+  const uint32_t f8_raw_lane = (uint32_t)(uintptr_t)(const lds_void*)lds.raw + kF8Wave * wid + 16 * lane;
+  auto f8_sc_addr = [&](int j, int ln) -> uint32_t {
+    const int u = f8_unit(j, ln);
+    return (uint32_t)(uintptr_t)(const lds_void*)lds.raw_sc + 256 * wid + 4 * ((u / 36) * G + f8_group(u % 36));
+  };
+  // LDS byte offset (in a bf16 tile) of the low half of unit j; the high
+  // half sits 16 bytes away (the two chunks 2 ch, 2 ch + 1 differ in the
+  // lowest bit of their swizzled position)
+  auto f8_dst = [&](int j, int ln) -> uint32_t {
+    const int u = f8_unit(j, ln);
+    return (uint32_t)tile_off(8 * wid + u / 36, 2 * (u % 36));
+  };
+  // four codes of a unit, scaled (block scale x E4M3 value), as bf16
+  auto f8_quarter = [](int code4, float sc, bf16x4& v) {
+    const auto x = __builtin_amdgcn_cvt_pk_f32_fp8(code4, false);
+    const auto y = __builtin_amdgcn_cvt_pk_f32_fp8(code4, true);
+    v[0] = (__bf16)(x[0] * sc);
+    v[1] = (__bf16)(x[1] * sc);
+    v[2] = (__bf16)(y[0] * sc);
+    v[3] = (__bf16)(y[1] * sc);
   };
 
   // ---------------------------------------------------------------- operand reads
@@ -515,6 +634,114 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     }
     return s0;
   };
+  // FP8: the same logits, with the next tile's dequantisation into the bf16
+  // slot `D` and the gathers of the tile after it (do_ld, row ids from tile
+  // `ld_tile`) between the MFMAs, on the schedule described at
+  // sfa_f8_schedule_ok.
+  auto logits_f8 = [&](const char* C, const char* D, bool do_ld, int ld_tile) -> f32x16 {
+    const uint32_t c = lds_addr(C), d = lds_addr(D);
+    bf16x8 av[KS];
+    i32x4 code[5];
+    float sc[5];
+    int rowv[6];
+    bf16x4 qv;
+    f32x16 s0 = (f32x16){};
+    const int ln = f8_lane();
+    const uint32_t raw_lane = f8_raw_lane;
+    const uint32_t rbase =
+        lds_addr(reinterpret_cast<const char*>(rows)) + 4 * (min(ld_tile, (ROWS / kTileRows) - 1) * kTileRows + 8 * wid);
+    // row (in the wave's eight) of unit j, or of this lane's scale entry (j = 5)
+    auto row_of = [&](int j) -> int {
+      const int sl = min(ln, 8 * G - 1);
+      return j < 5 ? f8_unit(j, ln) / 36 : (G == 1 ? sl : sl / 5);
+    };
+#define SLI_F8_READS(J)                                                                             \
+  do {                                                                                              \
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(code[J]) : "v"(raw_lane), "i"(1024 * (J))); \
+    asm volatile("ds_read_b32 %0, %1" : "=v"(sc[J]) : "v"(f8_sc_addr(J, ln)));                      \
+    asm volatile("ds_read_b32 %0, %1" : "=v"(rowv[J]) : "v"(rbase + 4 * row_of(J)));                \
+    if constexpr ((J) == 4) asm volatile("ds_read_b32 %0, %1" : "=v"(rowv[5]) : "v"(rbase + 4 * row_of(5))); \
+  } while (0)
+    SLI_WAIT_VMCNT(0);  // this wave's gathers of the next tile are in LDS
+    SLI_F8_READS(0);
+#pragma unroll
+    for (int k = 0; k < PDL; ++k) av_issue(c, k, av[k]);
+    static_for<KS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k + PDL < KS) av_issue(c, k + PDL, av[k + PDL]);
+      if constexpr (sfa_f8_read_at(k)) SLI_F8_READS((k + 3) / 7);
+      // unit j = (k - 1) / 7: quarter r converted and stored at step 1 + 7j + r
+      constexpr int j = (k - 1) / 7, r = (k - 1) % 7;
+      if constexpr (k >= 1 && j < 5 && r < 4) {
+        f8_quarter(code[j][r], sc[j], qv);
+        const uint32_t qa = ((d + f8_dst(j, ln)) ^ (r >= 2 ? 16u : 0u)) + 8u * (r & 1);
+        asm volatile("ds_write_b64 %0, %1" : : "v"(qa), "v"(qv) : "memory");
+      }
+      constexpr int w = sfa_f8_outstanding(PDL, k);
+      if constexpr (k == 0) {
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(av[0]), "+v"(code[0]), "+v"(sc[0]), "+v"(rowv[0]) : "i"(w));
+      } else if constexpr (k == 28) {
+        asm volatile("s_waitcnt lgkmcnt(%5)"
+                     : "+v"(av[k]), "+v"(code[4]), "+v"(sc[4]), "+v"(rowv[4]), "+v"(rowv[5])
+                     : "i"(w));
+      } else if constexpr (k >= 7 && k % 7 == 0) {
+        asm volatile("s_waitcnt lgkmcnt(%4)"
+                     : "+v"(av[k]), "+v"(code[k / 7]), "+v"(sc[k / 7]), "+v"(rowv[k / 7])
+                     : "i"(w));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(av[k]) : "i"(w));
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s0, 0, 0, 0);
+      // unit j's gather of the tile after next, into the bytes just read
+      if constexpr (k % 7 == 1 && k / 7 < 5) {
+        if (do_ld) {
+          constexpr int g = k / 7;
+          f8_pr[g] = rowv[g] >= 0 ? rowv[g] : fb_row;
+          f8_load(g, ln);
+        }
+      }
+      if constexpr (k == 29) {
+        if (do_ld) {
+          f8_pr[5] = rowv[5] >= 0 ? rowv[5] : fb_row;
+          f8_load(5, ln);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#undef SLI_F8_READS
+    return s0;
+  };
+  // FP8 prologue: tile 0 gathered, awaited and converted in one go
+  auto f8_convert_all = [&](const char* D) {
+    const uint32_t d = lds_addr(D);
+    const int ln = f8_lane();
+    i32x4 code[5];
+    float sc[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      switch (j) {
+#define SLI_F8_RD(J)                                                                                  \
+  case J:                                                                                             \
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(code[J]) : "v"(f8_raw_lane), "i"(1024 * J)); \
+    break;
+        SLI_F8_RD(0) SLI_F8_RD(1) SLI_F8_RD(2) SLI_F8_RD(3) SLI_F8_RD(4)
+#undef SLI_F8_RD
+      }
+      asm volatile("ds_read_b32 %0, %1" : "=v"(sc[j]) : "v"(f8_sc_addr(j, ln)));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(code[0]), "+v"(code[1]), "+v"(code[2]), "+v"(code[3]), "+v"(code[4]), "+v"(sc[0]),
+                   "+v"(sc[1]), "+v"(sc[2]), "+v"(sc[3]), "+v"(sc[4]));
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 qv;
+        f8_quarter(code[j][q], sc[j], qv);
+        const uint32_t qa = ((d + f8_dst(j, ln)) ^ (q >= 2 ? 16u : 0u)) + 8u * (q & 1);
+        asm volatile("ds_write_b64 %0, %1" : : "v"(qa), "v"(qv) : "memory");
+      }
+  };
   // Output product O^T[d, head] += C^T[d, pos] . P^T[pos, head] of the
   // previous tile (do_pv) for this wave's 128 columns and every head, with the
   // current tile's softmax stages (do_sm) interleaved between its MFMAs.  MFMA
@@ -523,7 +750,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // sfa_pv_wait.
   auto outprod = [&](const char* C, bool do_pv, const f32x16& sv, bool do_sm, int ld_tile, const int (&pr)[4]) {
     const uint32_t c = lds_addr(C) + 8192 * wid;
-    const int ld_row = tile_row(ld_tile, pr);
+    const char* const ld_src = row_src(tile_row(ld_tile, pr));
     const bool do_ld = ld_tile < tiles;
     char* const ld_dst = ring(ld_tile) + 1024 * wid_s;
     bf16x4 lo[8], hi[8];
@@ -561,8 +788,8 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
       // The next tile's loads go between these independent MFMAs, one every
       // third step (four waves then issue one about every 25 cycles, within
       // the ~15 cycles per direct-to-LDS load the CU accepts).
-      if constexpr (j % 3 == 1 && j / 3 < DPW) {
-        if (do_ld) load_one(ld_dst, ld_row, j / 3);
+      if constexpr (!F8 && j % 3 == 1 && j / 3 < DPW) {
+        if (do_ld) load_one(ld_dst, ld_src, j / 3);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -575,16 +802,36 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // The prologue always issues tiles 0 and 1 (past the last tile with the
   // fallback row), so the count is exact: waiting for all but those loads
   // completes the q loads issued before them, and the loop needs no wait for q.
-  issue(0);
-  issue(1);
-  SLI_WAIT_VMCNT(2 * DPW);
+  // FP8: tile 0 is gathered and converted here, tile 1 gathered; iteration
+  // t converts tile t + 1 (gathered during iteration t - 1) inside its logits
+  // and gathers tile t + 2 there.  Three bf16 slots: the logits' tile, the
+  // output product's (the one before) and the one being converted.
+  if constexpr (F8) {
+    if (tiles > 0) {
+      f8_rows(0);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) f8_load(j, lane);
+      SLI_WAIT_VMCNT(0);
+      f8_convert_all(ring(0));
+      if (tiles > 1) {
+        f8_rows(1);
+#pragma unroll
+        for (int j = 0; j < 6; ++j) f8_load(j, lane);
+      }
+    }
+  } else {
+    issue(0);
+    issue(1);
+    SLI_WAIT_VMCNT(2 * DPW);
+  }
   // row ids of the tile loaded next, and the valid-entry mask of the tile
   // consumed next, both read one iteration ahead
   int pr_next[4] = {0, 0, 0, 0};
-  if (2 < tiles) tile_rows(2, pr_next);
+  if (!F8 && 2 < tiles) tile_rows(2, pr_next);
   uint32_t vmask = tiles > 0 ? (uint32_t)__ballot(rows[n] >= 0) : 0u;
   auto step = [&](int tile, bool prev) {
-    if (tile + 1 < tiles) {
+    if constexpr (F8) {
+    } else if (tile + 1 < tiles) {
       SLI_WAIT_VMCNT(DPW);
     } else {
       SLI_WAIT_VMCNT(0);
@@ -600,8 +847,15 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
       apply_rescale(tile - 1);
     }
     const int pr[4] = {pr_next[0], pr_next[1], pr_next[2], pr_next[3]};
-    const f32x16 sv = logits(ring(tile));
-    if (tile + 3 < tiles) tile_rows(tile + 3, pr_next);
+    f32x16 sv;
+    if constexpr (F8) {
+      // (tile + 1 is converted even past the last tile, into a free slot, so
+      // that the schedule's LDS operation count never changes)
+      sv = logits_f8(ring(tile), ring(tile + 1), tile + 2 < tiles, tile + 2);
+    } else {
+      sv = logits(ring(tile));
+      if (tile + 3 < tiles) tile_rows(tile + 3, pr_next);
+    }
     const uint32_t vm_next = tile + 1 < tiles ? (uint32_t)__ballot(rows[(tile + 1) * kTileRows + n] >= 0) : 0u;
     outprod(ring(tile - 1), prev, sv, true, tile + 2, pr);
     sm_finish(vmask);
@@ -633,23 +887,24 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   constexpr int kStageRow = 1040;
-  {
-    float inv[NW];
+  constexpr int NSTAGE = F8 ? 3 : NW;  // head blocks staged at once
+  float inv[NW];
 #pragma unroll
-    for (int hb = 0; hb < NW; ++hb) inv[hb] = s_inv[32 * hb + n];
+  for (int hb = 0; hb < NW; ++hb) inv[hb] = s_inv[32 * hb + n];
+  auto stage_hb = [&](int hb, char* dst) {
 #pragma unroll
-    for (int hb = 0; hb < NW; ++hb)
+    for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * (4 * wid + mm) + 8 * q4 + 4 * half;
+        bf16x4 v4;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * (4 * wid + mm) + 8 * q4 + 4 * half;
-          bf16x4 v4;
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[4 * mm + hb][4 * q4 + i] * inv[hb]);
+        *reinterpret_cast<bf16x4*>(dst + n * kStageRow + 2 * d) = v4;
+      }
+  };
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[4 * mm + hb][4 * q4 + i] * inv[hb]);
-          *reinterpret_cast<bf16x4*>(ring(hb) + n * kStageRow + 2 * d) = v4;
-        }
-  }
+  for (int hb = 0; hb < NSTAGE; ++hb) stage_hb(hb, ring(hb));
   const size_t th = (size_t)t * a.H + head;
   const size_t ps = ((size_t)t * a.n_splits + split) * a.H + head;
   if (head_ok && half == 0) {
@@ -665,6 +920,34 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();  // head block wid's rows were staged by every wave
+  if constexpr (F8) {
+    // head blocks 0..2 by waves 0..2, then head block 3 through slot 0
+    const int hb = wid;
+    const int rows_out = min(32, a.H - 32 * hb);
+    __bf16* obase = whole ? static_cast<__bf16*>(a.out) + ((size_t)t * a.H + 32 * hb) * 512
+                          : a.part_o + (((size_t)t * a.n_splits + split) * a.H + 32 * hb) * 512;
+    if (hb < NSTAGE) {
+      const char* stage = ring(hb);
+#pragma unroll 4
+      for (int r = 0; r < rows_out; ++r) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(stage + r * kStageRow + 16 * lane);
+        *reinterpret_cast<i32x4*>(obase + (size_t)r * 512 + 8 * lane) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();  // slot 0 read out
+    stage_hb(NW - 1, ring(0));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    if (hb == NW - 1) {
+#pragma unroll 4
+      for (int r = 0; r < rows_out; ++r) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(ring(0) + r * kStageRow + 16 * lane);
+        *reinterpret_cast<i32x4*>(obase + (size_t)r * 512 + 8 * lane) = v;
+      }
+    }
+    return;
+  }
   const char* stage = ring(wid);
   const int rows_out = min(32, a.H - 32 * wid);
   __bf16* obase = whole ? static_cast<__bf16*>(a.out) + ((size_t)t * a.H + 32 * wid) * 512

@@ -71,6 +71,12 @@ SMALL = {
     "fp8r_g4_mtp2": dict(seed=26, B=2, n_q=2, seq_lens=[3000, 700], top_k=256, H=128, idx_fmt="mxfp8",
                          kv_fmt="fp8r", kv_groups=4),
     # FP8 latent with 64 heads: one workgroup per token slice, both 32-head groups in it
+    # FP8 rows of 576 bytes with 128 heads: the all-heads kernel (ragged
+    # slices, several tiles per split, both scale layouts)
+    "fp8_g1_h128_ragged": dict(seed=40, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=700, H=128, idx_fmt="fp8",
+                               kv_fmt="fp8", kv_groups=1),
+    "fp8_g5_h128_mtp2_tiles": dict(seed=41, B=32, n_q=2, seq_lens=[1200 + 97 * i for i in range(32)], top_k=1000,
+                                   H=128, idx_fmt="fp8", kv_fmt="fp8", kv_groups=5),
     "fp8_h64_ragged": dict(seed=27, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=520, H=64, idx_fmt="fp8",
                            kv_fmt="fp8", kv_groups=1),
     "fp8r_h64_mtp2": dict(seed=28, B=2, n_q=2, seq_lens=[2200, 333], top_k=300, H=64, idx_fmt="fp8",
@@ -127,6 +133,36 @@ def test_small_cases_full_path(li, name):
     ores = oracle.run_tokens(case, tokens)
     _check_indices(case, idx, tokens, ores)
     _check_attention(case, out, lse, tokens, ores)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_attention_pool_beyond_4gib(li, fmt):
+    # the same rows placed past 4.5 GiB of pool: 64-bit row addresses in the
+    # all-heads attention kernels give identical results
+    case = synth.Case(seed=42, B=2, n_q=1, seq_lens=[3000, 1700], top_k=512, H=128,
+                      **({} if fmt == "bf16" else dict(idx_fmt="fp8", kv_fmt="fp8", kv_groups=5)))
+    g = GpuCase(case)
+    idx = g.score_topk(li)
+    out, lse = g.attend(li, idx)
+    torch.cuda.synchronize()
+    row_bytes = 1152 if fmt == "bf16" else 576
+    p0 = -(-(9 << 29) // (64 * row_bytes))  # pages before the case's own
+    NP = g.kv_pool.shape[0]
+    big = torch.zeros((p0 + NP,) + tuple(g.kv_pool.shape[1:]), dtype=g.kv_pool.dtype, device="cuda")
+    big[p0:] = g.kv_pool
+    big_sc = None
+    if g.kv_scales is not None:
+        big_sc = torch.ones((p0 + NP,) + tuple(g.kv_scales.shape[1:]), dtype=torch.float32, device="cuda")
+        big_sc[p0:] = g.kv_scales
+    out2, lse2 = li.sfa_decode(g.mla_q, big, idx, g.seq_lens, g.block_table + p0, case.sm_scale, kv_scales=big_sc)
+    torch.cuda.synchronize()
+    assert big.numel() * big.element_size() > (1 << 32)
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
+    tokens = list(range(case.T))
+    ores = oracle.run_tokens(case, tokens)
+    _check_attention(case, out2.float().cpu().numpy(), lse2.cpu().numpy(), tokens, ores)
+    del big, big_sc
+    torch.cuda.empty_cache()
 
 
 def test_ties_break_to_lower_position(li):
