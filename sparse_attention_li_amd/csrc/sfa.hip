@@ -8,6 +8,12 @@
 //     l_j = sm_scale * q[t,h,:] . c[idx_j,:],   p = softmax_j(l),
 //     o[t,h,:] = sum_j p_j c[idx_j, 0:512],     lse[t,h] = log sum_j exp(l_j).
 //
+// Tokens with 65 to 128 heads over bf16 rows or FP8 rows of 576 bytes run
+// the all-heads kernels (sfa_bf16_kernel, sfa_f8_kernel: the body in
+// sfa_bf16_body.h, one workgroup per token and split holding every head, so
+// each selected row is gathered once per split).  The rest (up to 64 heads,
+// or FP8 rows with a bf16 rope) run the generic kernel below.
+//
 // Decomposition.  A workgroup owns one token, a block of up to 64 heads and a
 // contiguous slice of the token's index row (a "split").  Each 32-head group
 // is handled by WPH waves: for the logits each takes 1/WPH of the 576-wide

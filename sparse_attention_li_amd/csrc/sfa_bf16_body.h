@@ -1,7 +1,9 @@
-// Sparse MLA attention over bf16 latent rows, every head (up to 128) of a
-// token in one four-wave workgroup: the device body shared by the attention
-// launch (sfa.hip) and the single-launch decode step (decode_step.hip).
-// What it computes and the split merge are described in sfa.hip.
+// Sparse MLA attention over bf16 latent rows, or FP8 rows of 576 bytes
+// (E4M3 codes with block scales, converted to bf16 in LDS), every head (up
+// to 128) of a token in one four-wave workgroup: the device body shared by
+// the attention launches (sfa.hip) and the single-launch decode step
+// (decode_step.hip).  What it computes and the split merge are described in
+// sfa.hip.
 #pragma once
 
 #include <type_traits>
