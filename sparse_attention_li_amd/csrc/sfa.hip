@@ -427,6 +427,7 @@ __global__ __launch_bounds__(256) void sfa_f8_kernel(const SfaArgs a) {
   __shared__ __attribute__((aligned(128))) char slot2[kTileBytes];
   __shared__ __attribute__((aligned(128))) char raw[4 * kF8Wave];
   __shared__ __attribute__((aligned(128))) char raw_sc[4 * 256];
+  __shared__ __attribute__((aligned(128))) char qsave[4 * kF8QLds * 1024];
   __shared__ __attribute__((aligned(128))) char pbuf[4 * 2 * 64 * 16];
   __shared__ int rows[kMaxSplitRows];
   const int x = blockIdx.x & 7, g = blockIdx.x >> 3;
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(256) void sfa_f8_kernel(const SfaArgs a) {
   const int split = g % a.n_splits;
   if (t >= a.T) return;
   sfa_bf16_body<4, kMaxSplitRows, false, true>(
-      a, SfaBf16Lds{slot0, slot1, slot2, nullptr, pbuf, rows, raw, raw_sc}, t, split);
+      a, SfaBf16Lds{slot0, slot1, slot2, nullptr, pbuf, rows, raw, raw_sc, qsave}, t, split);
 }
 
 // FP8 rows of 576 bytes, every head of the token (65 to 128) in one workgroup.

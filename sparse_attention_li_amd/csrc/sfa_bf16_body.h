@@ -100,8 +100,10 @@ struct SfaBf16Lds {
   int* rows;   // ROWS entries
   char* raw = nullptr;
   char* raw_sc = nullptr;
+  char* qsave = nullptr;  // FP8: the first kF8QLds k-steps' q operands (4 x kF8QLds x 1 KiB)
 };
 constexpr int kF8Wave = 5 * 1024;  // raw bytes per wave: its 8 rows x 576 (4.5 KiB) + padding
+constexpr int kF8QLds = 3;         // q operands the FP8 logits read from LDS (registers for the conversion)
 
 // Schedule of the dequantisation that the FP8 variant interleaves with the
 // 36 logit MFMAs (steps 0..35) of the current tile.  Unit j (of five per
@@ -112,7 +114,9 @@ constexpr int kF8Wave = 5 * 1024;  // raw bytes per wave: its 8 rows x 576 (4.5 
 // unit 4) and awaited at step 7j; its gather of the tile after next goes out
 // at step 7j + 1, into the bytes just read, and the scale gather at step 29,
 // after the last scale read.  DS operations in issue order: before step 0
-// unit 0's three reads and the first PDL logit operand reads; at step s the
+// unit 0's three reads, the reads of the first kF8QLds k-steps' q operands
+// (kept in LDS: their registers hold the conversion) and the first PDL logit
+// operand reads; at step s the
 // operand read of k-step s + PDL, then a unit's reads, then the step's store.
 // Each step's wait leaves in flight only operations issued after everything
 // that step and the next one use.
@@ -123,13 +127,13 @@ __host__ __device__ constexpr int sfa_f8_ops_at(int pdl, int s) {
   return (s + pdl < 36 ? 1 : 0) + sfa_f8_reads_at(s) + (sfa_f8_store_at(s) ? 1 : 0);
 }
 __host__ __device__ constexpr int sfa_f8_ops_before(int pdl, int s) {
-  int n = 3 + pdl;
+  int n = 3 + kF8QLds + pdl;
   for (int i = 0; i < s; ++i) n += sfa_f8_ops_at(pdl, i);
   return n;
 }
 // position of the last operation the wait at step k must see completed
 __host__ __device__ constexpr int sfa_f8_need(int pdl, int k) {
-  int need = k < pdl ? 3 + k : sfa_f8_ops_before(pdl, k - pdl);  // logit operand k
+  int need = k < pdl ? 3 + kF8QLds + k : sfa_f8_ops_before(pdl, k - pdl);  // logit operand k
   if (k >= 7 && k <= 28 && k % 7 == 0) {  // unit k / 7: its reads at step k - 3
     const int idx = sfa_f8_ops_before(pdl, k - 3) + (k - 3 + pdl < 36 ? 1 : 0) + sfa_f8_reads_at(k - 3) - 1;
     need = need > idx ? need : idx;
@@ -319,11 +323,14 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
 
   // FP8 rows: 576 bytes = 36 16-byte units of E4M3 codes (512 latent, 64
   // rope), with kv_groups f32 block scales per row kept apart.  Wave w
-  // gathers its own rows 8w .. 8w+7 of a tile (units in order, lane l of load
-  // j taking unit l + 64 j; the fifth load's upper lanes fetch the last unit
-  // again into padding) and their scales into its part of the raw slot, and
-  // later converts exactly those bytes into the bf16 tile: a wave never waits
-  // for another wave's gather, and the raw slot needs no barrier.
+  // gathers its own rows 8w .. 8w+7 of a tile (lane l, h = l / 32, c = l % 32:
+  // loads j = 0..3 take latent unit c of row h + 2j, load 4 rope unit
+  // 32 + l % 4 of row (l % 32) / 4, its upper lanes fetching the lower lanes'
+  // units again into padding) and their scales into its part of the raw slot,
+  // and later converts exactly those bytes into the bf16 tile: a wave never
+  // waits for another wave's gather, and the raw slot needs no barrier.  (The
+  // mapping keeps the per-unit offsets to shifts and masks: the conversion
+  // runs between dependent MFMAs, where every vector instruction counts.)
   // (the per-lane unit offsets are recomputed where used, from a lane index
   // the compiler cannot hoist: kept live across the loop they would push the
   // q operands out of registers)
@@ -333,7 +340,9 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     asm volatile("" : "+v"(l));
     return l;
   };
-  auto f8_unit = [](int j, int ln) -> int { return j < 4 ? ln + 64 * j : min(256 + ln, 287); };
+  // row (in the wave's eight) and 16-byte unit of this lane's load j
+  auto f8_row = [](int j, int ln) -> int { return j < 4 ? (ln >> 5) + 2 * j : (ln & 31) >> 2; };
+  auto f8_ch = [](int j, int ln) -> int { return j < 4 ? (ln & 31) : 32 + (ln & 3); };
   // block scale of a unit (units 32..35 are the rope codes, scale group 4)
   auto f8_group = [&](int ch) -> int { return G == 1 ? 0 : min(ch >> 3, 4); };
   // this lane's scale entry: row 8w + sl / G, group sl % G (sl = min(lane, 8G - 1))
@@ -342,7 +351,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     const int ln = f8_lane(), sl = min(ln, 8 * G - 1);
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int rw = j < 5 ? f8_unit(j, ln) / 36 : (G == 1 ? sl : sl / 5);
+      const int rw = j < 5 ? f8_row(j, ln) : (G == 1 ? sl : sl / 5);
       const int pr = tile < tiles ? rows[tile * kTileRows + 8 * wid + rw] : -1;
       f8_pr[j] = pr >= 0 ? pr : fb_row;
     }
@@ -350,8 +359,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // gather j (0..4: codes, 5: scales) of the tile whose rows f8_rows resolved
   auto f8_load = [&](int j, int ln) {
     if (j < 5) {
-      const int u = f8_unit(j, ln);
-      const char* src = static_cast<const char*>(a.kv) + (size_t)f8_pr[j] * 576 + 16 * (u % 36);
+      const char* src = static_cast<const char*>(a.kv) + (size_t)f8_pr[j] * 576 + 16 * f8_ch(j, ln);
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds.raw + kF8Wave * wid_s + 1024 * j), 16, 0, 0);
     } else {
       const int sl = min(ln, 8 * G - 1);
@@ -361,15 +369,21 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   };
   const uint32_t f8_raw_lane = (uint32_t)(uintptr_t)(const lds_void*)lds.raw + kF8Wave * wid + 16 * lane;
   auto f8_sc_addr = [&](int j, int ln) -> uint32_t {
-    const int u = f8_unit(j, ln);
-    return (uint32_t)(uintptr_t)(const lds_void*)lds.raw_sc + 256 * wid + 4 * ((u / 36) * G + f8_group(u % 36));
+    return (uint32_t)(uintptr_t)(const lds_void*)lds.raw_sc + 256 * wid +
+           4 * (f8_row(j, ln) * G + f8_group(f8_ch(j, ln)));
   };
   // LDS byte offset (in a bf16 tile) of the low half of unit j; the high
   // half sits 16 bytes away (the two chunks 2 ch, 2 ch + 1 differ in the
-  // lowest bit of their swizzled position)
+  // lowest bit of their swizzled position).  For the latent loads this is
+  // tile_off(8w + h + 2j, 2c) with the swizzle of row h + 2j written out:
+  // 2h + 4 (j % 2) + j / 2, bit-disjoint from 2h's neighbours, so one XOR.
   auto f8_dst = [&](int j, int ln) -> uint32_t {
-    const int u = f8_unit(j, ln);
-    return (uint32_t)tile_off(8 * wid + u / 36, 2 * (u % 36));
+    if (j < 4) {
+      const int c = ln & 31, h = ln >> 5, kj = 4 * (j & 1) + (j >> 1);
+      return (uint32_t)(16 * (256 * (c >> 2) + 64 * wid + 8 * h + 16 * j + (((2 * (c & 3)) ^ (2 * h)) ^ kj)));
+    }
+    const int l = ln & 31;
+    return (uint32_t)tile_off(8 * wid + (l >> 2), 2 * (32 + (l & 3)));
   };
   // four codes of a unit, scaled (block scale x E4M3 value), as bf16
   auto f8_quarter = [](int code4, float sc, bf16x4& v) {
@@ -655,7 +669,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     // row (in the wave's eight) of unit j, or of this lane's scale entry (j = 5)
     auto row_of = [&](int j) -> int {
       const int sl = min(ln, 8 * G - 1);
-      return j < 5 ? f8_unit(j, ln) / 36 : (G == 1 ? sl : sl / 5);
+      return j < 5 ? f8_row(j, ln) : (G == 1 ? sl : sl / 5);
     };
 #define SLI_F8_READS(J)                                                                             \
   do {                                                                                              \
@@ -666,6 +680,13 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   } while (0)
     SLI_WAIT_VMCNT(0);  // this wave's gathers of the next tile are in LDS
     SLI_F8_READS(0);
+    bf16x8 ql[kF8QLds];
+    {
+      const uint32_t qa = lds_addr(lds.qsave) + 1024 * kF8QLds * wid + 16 * ln;
+      asm volatile("ds_read_b128 %0, %1" : "=v"(ql[0]) : "v"(qa));
+      asm volatile("ds_read_b128 %0, %1 offset:1024" : "=v"(ql[1]) : "v"(qa));
+      asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(ql[2]) : "v"(qa));
+    }
 #pragma unroll
     for (int k = 0; k < PDL; ++k) av_issue(c, k, av[k]);
     static_for<KS>([&](auto kc) {
@@ -681,7 +702,9 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
       }
       constexpr int w = sfa_f8_outstanding(PDL, k);
       if constexpr (k == 0) {
-        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(av[0]), "+v"(code[0]), "+v"(sc[0]), "+v"(rowv[0]) : "i"(w));
+        asm volatile("s_waitcnt lgkmcnt(%7)"
+                     : "+v"(av[0]), "+v"(code[0]), "+v"(sc[0]), "+v"(rowv[0]), "+v"(ql[0]), "+v"(ql[1]), "+v"(ql[2])
+                     : "i"(w));
       } else if constexpr (k == 28) {
         asm volatile("s_waitcnt lgkmcnt(%5)"
                      : "+v"(av[k]), "+v"(code[4]), "+v"(sc[4]), "+v"(rowv[4]), "+v"(rowv[5])
@@ -693,7 +716,11 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
       } else {
         asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(av[k]) : "i"(w));
       }
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s0, 0, 0, 0);
+      if constexpr (k < kF8QLds) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], ql[k], s0, 0, 0, 0);
+      } else {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k], qb[k], s0, 0, 0, 0);
+      }
       // unit j's gather of the tile after next, into the bytes just read
       if constexpr (k % 7 == 1 && k / 7 < 5) {
         if (do_ld) {
@@ -810,6 +837,10 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // output product's (the one before) and the one being converted.
   if constexpr (F8) {
     if (tiles > 0) {
+#pragma unroll
+      for (int k = 0; k < kF8QLds; ++k)
+        *reinterpret_cast<bf16x8*>(lds.qsave + 1024 * (kF8QLds * wid + k) + 16 * lane) = qb[k];
+      asm volatile("" : : : "memory");  // (stored before the explicit reads of them)
       f8_rows(0);
 #pragma unroll
       for (int j = 0; j < 6; ++j) f8_load(j, lane);
