@@ -82,13 +82,12 @@ int spin_max() { return g_patience.load(std::memory_order_relaxed); }
 
 // Splits of the index row so that about one workgroup per CU is busy (an
 // attention workgroup fills a CU: one wave per SIMD).  Workgroups hold every
-// head of a token (65 to 128 heads; bf16 rows and FP8 rows of 576 bytes), or
-// a block of up to 64 heads (FP8 rows with a bf16 rope).  Small calls
+// head of a token (65 to 128 heads), or a block of 32 or 64.  Small calls
 // split down to one 32-row tile per workgroup (batch 1 x 2048, top-K 256:
 // 8 splits, 16.8 -> 13.5 us against two-tile splits).
-void sfa_shape(int T, int H, int top_k, bool rope16, int& n_splits, int& split_len) {
+void sfa_shape(int T, int H, int top_k, int& n_splits, int& split_len) {
   const int cus = device_cus();
-  const int hpb = sli::sfa_heads_per_block(H, rope16);
+  const int hpb = sli::sfa_heads_per_block(H);
   const int head_blocks = (H + hpb - 1) / hpb;
   const int per_split = T * head_blocks;
   int s = std::max(1, (cus + per_split - 1) / per_split);
@@ -318,13 +317,9 @@ li_status li_score_topk(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_
 
 size_t sfa_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t top_k) {
   if (num_tokens <= 0 || num_heads <= 0 || top_k <= 0) return 0;
-  size_t need = 0;
-  for (bool rope16 : {false, true}) {
-    int s, len;
-    sfa_shape(num_tokens, num_heads, top_k, rope16, s, len);
-    need = std::max(need, sfa_partials_bytes(num_tokens, num_heads, s));
-  }
-  return need;
+  int s, len;
+  sfa_shape(num_tokens, num_heads, top_k, s, len);
+  return sfa_partials_bytes(num_tokens, num_heads, s);
 }
 
 static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* seq_lens, const int32_t* block_table,
@@ -338,7 +333,7 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
   const bool fp8 = kv_dtype != LI_BF16, rope16 = kv_dtype == LI_FP8_ROPE_BF16;
   const int T = num_seqs * q_per_seq;
   int s, len;
-  sfa_shape(T, num_heads, top_k, rope16, s, len);
+  sfa_shape(T, num_heads, top_k, s, len);
   sli::SfaArgs a;
   a.T = T;
   a.n_q = q_per_seq;
@@ -350,7 +345,7 @@ static li_status sfa_common(int32_t num_seqs, int32_t q_per_seq, const int32_t* 
   a.rope_bf16 = rope16 ? 1 : 0;
   a.n_splits = s;
   a.split_len = len;
-  a.head_blocks = (num_heads + sli::sfa_heads_per_block(num_heads, rope16) - 1) / sli::sfa_heads_per_block(num_heads, rope16);
+  a.head_blocks = (num_heads + sli::sfa_heads_per_block(num_heads) - 1) / sli::sfa_heads_per_block(num_heads);
   a.sm_scale = sm_scale;
   a.seq_lens = seq_lens;
   a.block_table = block_table;

@@ -115,6 +115,6 @@ hipError_t launch_idx_prefill(const IdxPrefillArgs& a, hipStream_t stream);
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_decode_step(const StepArgs& s, hipStream_t stream);
 hipError_t launch_validate_paged(const ValidateArgs& a, hipStream_t stream);
-int sfa_heads_per_block(int H, bool rope16);
+int sfa_heads_per_block(int H);
 
 }  // namespace sli

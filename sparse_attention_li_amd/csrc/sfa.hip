@@ -8,11 +8,10 @@
 //     l_j = sm_scale * q[t,h,:] . c[idx_j,:],   p = softmax_j(l),
 //     o[t,h,:] = sum_j p_j c[idx_j, 0:512],     lse[t,h] = log sum_j exp(l_j).
 //
-// Tokens with 65 to 128 heads over bf16 rows or FP8 rows of 576 bytes run
-// the all-heads kernels (sfa_bf16_kernel, sfa_f8_kernel: the body in
-// sfa_bf16_body.h, one workgroup per token and split holding every head, so
-// each selected row is gathered once per split).  The rest (up to 64 heads,
-// or FP8 rows with a bf16 rope) run the generic kernel below.
+// Tokens with 65 to 128 heads run the all-heads kernels (sfa_bf16_kernel,
+// sfa_f8_kernel: the body in sfa_bf16_body.h, one workgroup per token and
+// split holding every head, so each selected row is gathered once per
+// split).  Up to 64 heads run the generic kernel below.
 //
 // Decomposition.  A workgroup owns one token, a block of up to 64 heads and a
 // contiguous slice of the token's index row (a "split").  Each 32-head group
@@ -418,9 +417,11 @@ static hipError_t launch_sfa_bf16(const SfaArgs& a, hipStream_t stream) {
   return e != hipSuccess ? e : launch_combine(a, stream);
 }
 
-// FP8 latent rows of 576 bytes (E4M3 codes, block scales apart), every head
-// of the token in one workgroup: the same body and block layout, with three
-// bf16 slots that the waves fill by converting their own gathered rows.
+// FP8 latent rows (E4M3 codes with block scales apart; R16: with the rope in
+// bf16), every head of the token in one workgroup: the same body and block
+// layout, with three bf16 slots that the waves fill by converting their own
+// gathered rows.
+template <bool R16>
 __global__ __launch_bounds__(256) void sfa_f8_kernel(const SfaArgs a) {
   __shared__ __attribute__((aligned(128))) char slot0[kTileBytes];
   __shared__ __attribute__((aligned(128))) char slot1[kTileBytes];
@@ -435,20 +436,22 @@ __global__ __launch_bounds__(256) void sfa_f8_kernel(const SfaArgs a) {
   const int t = x * tpx + g / a.n_splits;
   const int split = g % a.n_splits;
   if (t >= a.T) return;
-  sfa_bf16_body<4, kMaxSplitRows, false, true>(
+  sfa_bf16_body<4, kMaxSplitRows, false, true, R16>(
       a, SfaBf16Lds{slot0, slot1, slot2, nullptr, pbuf, rows, raw, raw_sc, qsave}, t, split);
 }
 
-// FP8 rows of 576 bytes, every head of the token (65 to 128) in one workgroup.
+// FP8 rows (576 bytes, or 640 with a bf16 rope), every head of the token
+// (65 to 128) in one workgroup.
+template <bool R16>
 static hipError_t launch_sfa_f8(const SfaArgs& a, hipStream_t stream) {
   dim3 grid(8 * ((a.T + 7) / 8) * a.n_splits);
-  hipLaunchKernelGGL(sfa_f8_kernel, grid, dim3(4 * 64), 0, stream, a);
+  hipLaunchKernelGGL((sfa_f8_kernel<R16>), grid, dim3(4 * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_combine(a, stream);
 }
 
 hipError_t launch_sfa(const SfaArgs& a, bool fp8, hipStream_t stream) {
-  if (fp8 && !a.rope_bf16 && a.H > 64) return launch_sfa_f8(a, stream);
+  if (fp8 && a.H > 64) return a.rope_bf16 ? launch_sfa_f8<true>(a, stream) : launch_sfa_f8<false>(a, stream);
   if (fp8 && a.rope_bf16)
     return a.H <= 32 ? launch_sfa_blocks<1, true, true>(a, stream) : launch_sfa_blocks<2, true, true>(a, stream);
   if (fp8) return a.H <= 32 ? launch_sfa_blocks<1, true>(a, stream) : launch_sfa_blocks<2, true>(a, stream);

@@ -169,7 +169,7 @@ __device__ __forceinline__ void sfa_load_q(const SfaArgs& a, const int t, bf16x8
 // loaded this lane's q^T operands (sfa_load_q) into qpre; with `direct` the
 // result is the token's output, else the partial of slot `split`, written
 // through to memory for the workgroup that merges it.
-template <int NW, int ROWS, bool FUSED, bool F8 = false>
+template <int NW, int ROWS, bool FUSED, bool F8 = false, bool R16 = false>
 __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds& lds, const int t, const int split,
                                               const int own_cnt = 0, const bool direct = false,
                                               const bf16x8* qpre = nullptr) {
@@ -322,11 +322,13 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   };
 
   // FP8 rows: 576 bytes = 36 16-byte units of E4M3 codes (512 latent, 64
-  // rope), with kv_groups f32 block scales per row kept apart.  Wave w
-  // gathers its own rows 8w .. 8w+7 of a tile (lane l, h = l / 32, c = l % 32:
-  // loads j = 0..3 take latent unit c of row h + 2j, load 4 rope unit
-  // 32 + l % 4 of row (l % 32) / 4, its upper lanes fetching the lower lanes'
-  // units again into padding) and their scales into its part of the raw slot,
+  // rope), with kv_groups f32 block scales per row kept apart; with R16, 640
+  // bytes = 32 units of latent codes + 8 units of bf16 rope (copied as they
+  // are).  Wave w gathers its own rows 8w .. 8w+7 of a tile (lane l,
+  // h = l / 32, c = l % 32: loads j = 0..3 take latent unit c of row h + 2j,
+  // load 4 rope unit 32 + l % 4 of row (l % 32) / 4, its upper lanes fetching
+  // the lower lanes' units again into padding; with R16 rope unit 32 + l % 8
+  // of row l / 8) and their scales into its part of the raw slot,
   // and later converts exactly those bytes into the bf16 tile: a wave never
   // waits for another wave's gather, and the raw slot needs no barrier.  (The
   // mapping keeps the per-unit offsets to shifts and masks: the conversion
@@ -341,17 +343,21 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     return l;
   };
   // row (in the wave's eight) and 16-byte unit of this lane's load j
-  auto f8_row = [](int j, int ln) -> int { return j < 4 ? (ln >> 5) + 2 * j : (ln & 31) >> 2; };
-  auto f8_ch = [](int j, int ln) -> int { return j < 4 ? (ln & 31) : 32 + (ln & 3); };
-  // block scale of a unit (units 32..35 are the rope codes, scale group 4)
+  auto f8_row = [](int j, int ln) -> int { return j < 4 ? (ln >> 5) + 2 * j : (R16 ? ln >> 3 : (ln & 31) >> 2); };
+  auto f8_ch = [](int j, int ln) -> int { return j < 4 ? (ln & 31) : 32 + (R16 ? ln & 7 : ln & 3); };
+  constexpr int F8_ROW = R16 ? 640 : 576;
+  // block scale of a unit (units 32..35 are the rope codes, scale group 4;
+  // a bf16 rope unit has none, and reads an unused entry)
   auto f8_group = [&](int ch) -> int { return G == 1 ? 0 : min(ch >> 3, 4); };
-  // this lane's scale entry: row 8w + sl / G, group sl % G (sl = min(lane, 8G - 1))
+  // this lane's scale entry: row 8w + sl / G, group sl % G (sl = min(lane, 8G - 1), G = 1, 4 or 5)
+  auto f8_sl_row = [&](int sl) -> int { return G == 1 ? sl : (G == 4 ? sl >> 2 : sl / 5); };
+  auto f8_sl_grp = [&](int sl) -> int { return G == 1 ? 0 : (G == 4 ? sl & 3 : sl % 5); };
   int f8_pr[6];  // pool rows of this lane's five units and of its scale entry
   auto f8_rows = [&](int tile) {
     const int ln = f8_lane(), sl = min(ln, 8 * G - 1);
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int rw = j < 5 ? f8_row(j, ln) : (G == 1 ? sl : sl / 5);
+      const int rw = j < 5 ? f8_row(j, ln) : f8_sl_row(sl);
       const int pr = tile < tiles ? rows[tile * kTileRows + 8 * wid + rw] : -1;
       f8_pr[j] = pr >= 0 ? pr : fb_row;
     }
@@ -359,11 +365,11 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
   // gather j (0..4: codes, 5: scales) of the tile whose rows f8_rows resolved
   auto f8_load = [&](int j, int ln) {
     if (j < 5) {
-      const char* src = static_cast<const char*>(a.kv) + (size_t)f8_pr[j] * 576 + 16 * f8_ch(j, ln);
+      const char* src = static_cast<const char*>(a.kv) + (size_t)f8_pr[j] * F8_ROW + 16 * f8_ch(j, ln);
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds.raw + kF8Wave * wid_s + 1024 * j), 16, 0, 0);
     } else {
       const int sl = min(ln, 8 * G - 1);
-      const float* src = a.kv_scales + (size_t)f8_pr[5] * G + (G == 1 ? 0 : sl % 5);
+      const float* src = a.kv_scales + (size_t)f8_pr[5] * G + f8_sl_grp(sl);
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds.raw_sc + 256 * wid_s), 4, 0, 0);
     }
   };
@@ -382,8 +388,14 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
       const int c = ln & 31, h = ln >> 5, kj = 4 * (j & 1) + (j >> 1);
       return (uint32_t)(16 * (256 * (c >> 2) + 64 * wid + 8 * h + 16 * j + (((2 * (c & 3)) ^ (2 * h)) ^ kj)));
     }
+    if constexpr (R16) return (uint32_t)tile_off(8 * wid + (ln >> 3), 64 + (ln & 7));  // one bf16 chunk
     const int l = ln & 31;
     return (uint32_t)tile_off(8 * wid + (l >> 2), 2 * (32 + (l & 3)));
+  };
+  // half (r % 2) of a bf16 rope unit, unchanged
+  auto f8_rope_half = [](const i32x4& u, int r) -> bf16x4 {
+    const uint64_t v = (uint64_t)(uint32_t)u[2 * (r & 1)] | ((uint64_t)(uint32_t)u[2 * (r & 1) + 1] << 32);
+    return __builtin_bit_cast(bf16x4, v);
   };
   // four codes of a unit, scaled (block scale x E4M3 value), as bf16
   auto f8_quarter = [](int code4, float sc, bf16x4& v) {
@@ -669,7 +681,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
     // row (in the wave's eight) of unit j, or of this lane's scale entry (j = 5)
     auto row_of = [&](int j) -> int {
       const int sl = min(ln, 8 * G - 1);
-      return j < 5 ? f8_row(j, ln) : (G == 1 ? sl : sl / 5);
+      return j < 5 ? f8_row(j, ln) : f8_sl_row(sl);
     };
 #define SLI_F8_READS(J)                                                                             \
   do {                                                                                              \
@@ -696,8 +708,16 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
       // unit j = (k - 1) / 7: quarter r converted and stored at step 1 + 7j + r
       constexpr int j = (k - 1) / 7, r = (k - 1) % 7;
       if constexpr (k >= 1 && j < 5 && r < 4) {
-        f8_quarter(code[j][r], sc[j], qv);
-        const uint32_t qa = ((d + f8_dst(j, ln)) ^ (r >= 2 ? 16u : 0u)) + 8u * (r & 1);
+        uint32_t qa;
+        if constexpr (R16 && j == 4) {
+          // bf16 rope: the unit's two halves as they are (written twice, so
+          // that every unit takes four stores)
+          qv = f8_rope_half(code[4], r);
+          qa = d + f8_dst(j, ln) + 8u * (r & 1);
+        } else {
+          f8_quarter(code[j][r], sc[j], qv);
+          qa = ((d + f8_dst(j, ln)) ^ (r >= 2 ? 16u : 0u)) + 8u * (r & 1);
+        }
         asm volatile("ds_write_b64 %0, %1" : : "v"(qa), "v"(qv) : "memory");
       }
       constexpr int w = sfa_f8_outstanding(PDL, k);
@@ -766,8 +786,14 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaArgs& a, const SfaBf16Lds
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         bf16x4 qv;
-        f8_quarter(code[j][q], sc[j], qv);
-        const uint32_t qa = ((d + f8_dst(j, ln)) ^ (q >= 2 ? 16u : 0u)) + 8u * (q & 1);
+        uint32_t qa;
+        if (R16 && j == 4) {
+          qv = f8_rope_half(code[4], q);
+          qa = d + f8_dst(j, ln) + 8u * (q & 1);
+        } else {
+          f8_quarter(code[j][q], sc[j], qv);
+          qa = ((d + f8_dst(j, ln)) ^ (q >= 2 ? 16u : 0u)) + 8u * (q & 1);
+        }
         asm volatile("ds_write_b64 %0, %1" : : "v"(qa), "v"(qv) : "memory");
       }
   };

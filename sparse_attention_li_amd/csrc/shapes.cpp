@@ -34,9 +34,8 @@ bool idx_decode_xcd_local(int B, int n_chunks_max, int chunk, int cus) {
   return B >= 16 && n_chunks_max <= cus / 8 && (long long)B * n_chunks_max > cus;
 }
 
-// Heads per attention workgroup: every head of the token (65 to 128) for
-// bf16 rows and FP8 rows of 576 bytes, blocks of up to 64 heads for FP8 rows
-// with a bf16 rope or small head counts.
-int sfa_heads_per_block(int H, bool rope16) { return (rope16 || H <= 64) ? (H <= 32 ? 32 : 64) : 128; }
+// Heads per attention workgroup: every head of the token (65 to 128), or a
+// block of 32 or 64 for small head counts.
+int sfa_heads_per_block(int H) { return H <= 64 ? (H <= 32 ? 32 : 64) : 128; }
 
 }  // namespace sli

@@ -71,10 +71,12 @@ SMALL = {
     "fp8r_g4_mtp2": dict(seed=26, B=2, n_q=2, seq_lens=[3000, 700], top_k=256, H=128, idx_fmt="mxfp8",
                          kv_fmt="fp8r", kv_groups=4),
     # FP8 latent with 64 heads: one workgroup per token slice, both 32-head groups in it
-    # FP8 rows of 576 bytes with 128 heads: the all-heads kernel (ragged
-    # slices, several tiles per split, both scale layouts)
+    # FP8 rows with 128 heads: the all-heads kernel (ragged slices, several
+    # tiles per split, every scale layout, bf16 rope)
     "fp8_g1_h128_ragged": dict(seed=40, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=700, H=128, idx_fmt="fp8",
                                kv_fmt="fp8", kv_groups=1),
+    "fp8r_g1_h128_ragged": dict(seed=43, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=700, H=128, idx_fmt="fp8",
+                                kv_fmt="fp8r", kv_groups=1),
     "fp8_g5_h128_mtp2_tiles": dict(seed=41, B=32, n_q=2, seq_lens=[1200 + 97 * i for i in range(32)], top_k=1000,
                                    H=128, idx_fmt="fp8", kv_fmt="fp8", kv_groups=5),
     "fp8_h64_ragged": dict(seed=27, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=520, H=64, idx_fmt="fp8",
