@@ -135,3 +135,28 @@ def test_step_two_launch_shapes(li, name):
     idx, out, lse = _step(li, g)
     tokens = list(range(case.T))
     _check(case, idx, out, lse, tokens, oracle.run_tokens(case, tokens))
+
+
+def test_step_pool_beyond_4gib(li):
+    # the same pages placed past 4.5 GiB of latent pool (and past 1 GiB of
+    # key pool): 64-bit row addresses in the single-launch step give identical
+    # results
+    case = synth.Case(seed=44, B=4, n_q=1, seq_lens=[3000, 9000, 2000, 5000], top_k=512, H=128)
+    g = GpuCase(case)
+    idx, out, lse = _step(li, g)
+    p0 = -(-(9 << 29) // (64 * 1152))
+    NP = g.kv_pool.shape[0]
+    big_kv = torch.zeros((p0 + NP,) + tuple(g.kv_pool.shape[1:]), dtype=g.kv_pool.dtype, device="cuda")
+    big_kv[p0:] = g.kv_pool
+    big_k = torch.zeros((p0 + NP,) + tuple(g.k_pool.shape[1:]), dtype=g.k_pool.dtype, device="cuda")
+    big_k[p0:] = g.k_pool
+    assert big_kv.numel() * big_kv.element_size() > (1 << 32)
+    idx2, out2, lse2 = li.li_decode_step(g.q, g.w, big_k, g.mla_q, big_kv, g.seq_lens, g.block_table + p0,
+                                         case.top_k, case.sm_scale)
+    torch.cuda.synchronize()
+    assert (idx2.cpu().numpy() == idx).all()
+    assert np.array_equal(out2.float().cpu().numpy(), out) and np.array_equal(lse2.cpu().numpy(), lse)
+    tokens = list(range(case.T))
+    _check(case, idx, out, lse, tokens, oracle.run_tokens(case, tokens))
+    del big_kv, big_k
+    torch.cuda.empty_cache()
