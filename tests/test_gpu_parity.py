@@ -77,6 +77,12 @@ SMALL = {
                                kv_fmt="fp8", kv_groups=1),
     "fp8r_g1_h128_ragged": dict(seed=43, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=700, H=128, idx_fmt="fp8",
                                 kv_fmt="fp8r", kv_groups=1),
+    "fp8_h128_k1": dict(seed=45, B=2, n_q=1, seq_lens=[777, 1025], top_k=1, H=128, idx_fmt="fp8", kv_fmt="fp8",
+                        kv_groups=5),
+    "fp8r_h128_empty_mtp2": dict(seed=46, B=3, n_q=2, seq_lens=[2100, 0, 700], top_k=300, H=128, idx_fmt="fp8",
+                                 kv_fmt="fp8r", kv_groups=4),
+    "prefill_fp8_latent_h128": dict(seed=47, B=1, n_q=12, seq_lens=[3000], top_k=256, H=128, kv_fmt="fp8",
+                                    kv_groups=5),
     "fp8_g5_h128_mtp2_tiles": dict(seed=41, B=32, n_q=2, seq_lens=[1200 + 97 * i for i in range(32)], top_k=1000,
                                    H=128, idx_fmt="fp8", kv_fmt="fp8", kv_groups=5),
     "fp8_h64_ragged": dict(seed=27, B=3, n_q=1, seq_lens=[900, 2600, 4100], top_k=520, H=64, idx_fmt="fp8",
